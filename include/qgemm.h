@@ -1,0 +1,228 @@
+/*
+ * qgemm.h -- C ABI of libqgemm.so, a GEMM engine for AMD MI355X (gfx950).
+ *
+ * The engine computes
+ *
+ *     D = alpha * (A @ B) + beta * C
+ *
+ * with operands A, U, B, V, C, D, a caller-owned workspace and a stream, the
+ * operation and argument order stated on the page "InternLM Lmdeploy Gemm
+ * Interface" (Description; Signature of Gemm::Run; I/O Contract). U and V are
+ * the optional quantisation scale operands of that contract; the group-wise
+ * stepping of U/V along K follows the page "InternLM Lmdeploy Gemm
+ * MainloopSm80V2" (Description, quantisation group tracking).
+ *
+ * Conventions used throughout
+ *   - "B" is the operand stored N x K with K contiguous (row-major N x K), so
+ *     (A @ B)(i, j) = sum_k A[i, k] * B[j, k]. A is M x K row-major; C and D
+ *     are M x N row-major.
+ *   - All matrix pointers are DEVICE pointers on the handle's device. Layout
+ *     descriptors (qg_layout, qg_operation, qg_workspace) are HOST structs
+ *     read during the call only; the engine keeps no reference to them.
+ *   - Every call returns 0 on success (the page's "0 on success") or one of
+ *     the negative qg_status codes below. qg_run enqueues work on `stream`
+ *     and returns without synchronising; device faults surface at the
+ *     caller's next synchronisation. It never allocates or frees device
+ *     memory (the measure policy allocates nothing either; it synchronises).
+ *   - Accumulation is fp32 for float inputs and exact int32 for int8.
+ *   - Alignment: every device pointer and every row pitch (ld * element size)
+ *     must be a multiple of 16 bytes; K must keep rows 16-byte aligned too.
+ *
+ * Threading: one handle may be used from several host threads except under
+ * QG_POLICY_MEASURE (which mutates the dispatch cache and synchronises the
+ * stream). Runs that execute concurrently on the device need separate
+ * workspaces.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t, declared here so that the header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef struct qg_handle qg_handle;
+
+/* ---- status codes ------------------------------------------------------ */
+enum qg_status {
+  QG_OK = 0,
+  QG_ERR_INVALID_ARG = -1,  /* null handle/pointer, bad shape, inconsistent layouts */
+  QG_ERR_UNSUPPORTED = -2,  /* valid request this engine does not implement */
+  QG_ERR_ALIGNMENT = -3,    /* pointer or row pitch not 16-byte aligned */
+  QG_ERR_WORKSPACE = -4,    /* workspace missing or too small for the plan */
+  QG_ERR_NO_KERNEL = -5,    /* no registered kernel fits / REUSE policy missed the cache */
+  QG_ERR_HIP = -6,          /* a HIP runtime call failed */
+  QG_ERR_FORMAT = -7,       /* qg_import: malformed, truncated or foreign cache text */
+  QG_ERR_BUFFER_SMALL = -8  /* output buffer too small (the needed size is reported) */
+};
+
+/* ---- element types ------------------------------------------------------ */
+typedef enum qg_dtype {
+  QG_F32 = 0,
+  QG_F16 = 1,
+  QG_BF16 = 2,
+  QG_E4M3 = 3, /* OCP 8-bit float E4M3 ("fn": no infinities, max 448) */
+  QG_I8 = 4,
+  QG_I32 = 5,
+  QG_U4 = 6    /* unsigned 4-bit, packed 8 per uint32: element k = 8w + i in
+                  bits [4i, 4i+4) of word w of its row; ld counts words */
+} qg_dtype;
+
+typedef enum qg_order { QG_ROW_MAJOR = 0, QG_COL_MAJOR = 1 } qg_order;
+
+/* Describes one operand ("MatrixLayout" of the Run signature).
+ *   type, order  element type and storage order (only QG_ROW_MAJOR today).
+ *   rows, cols   logical shape. A: M x K, B: N x K, C/D: M x N,
+ *                U (fp8 A scales): ceil(M/group_mn) x ceil(K/group_k) fp32,
+ *                V (int4 scales): N x ceil(K/group_k) fp16,
+ *                V (fp8 B scales): ceil(N/group_mn) x ceil(K/group_k) fp32.
+ *                For a grouped problem rows of A/C/D/U is the total row count
+ *                and B/V give ONE group's shape.
+ *   ld           leading dimension (elements; uint32 words for QG_U4).
+ *   num          number of groups (MoE experts); 0 or 1 = plain GEMM.
+ *   offsets      grouped A/C/D/U: DEVICE int32 array of num+1 row offsets,
+ *                offsets[0] = 0, non-decreasing, offsets[num] <= rows; group e
+ *                owns rows [offsets[e], offsets[e+1]). May be empty groups.
+ *   stride       grouped B/V: elements (words) from group e to group e+1. */
+typedef struct qg_layout {
+  int32_t type;
+  int32_t order;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+  int32_t num;
+  int32_t reserved;
+  const int32_t* offsets;
+  int64_t stride;
+} qg_layout;
+
+/* ---- operation descriptor ("Dispatch policy, epilogue, quantization config") */
+typedef enum qg_policy {
+  QG_POLICY_DEFAULT = 0, /* cache hit (exact key, else nearest tuning bucket >= M), else heuristic */
+  QG_POLICY_MEASURE = 1, /* as DEFAULT on a hit; on an exact-key miss time the candidates
+                            on `stream` (synchronises), cache the fastest, then run it */
+  QG_POLICY_REUSE = 2,   /* cache only: a miss returns QG_ERR_NO_KERNEL */
+  QG_POLICY_FORCE = 3    /* use schedule / split_k / programs / kernel exactly as given */
+} qg_policy;
+
+typedef enum qg_epilogue { QG_EPI_ALPHA_BETA = 0 } qg_epilogue;
+
+typedef enum qg_quant_kind {
+  QG_QUANT_NONE = 0,
+  QG_QUANT_INT4_ZP = 1,   /* B only: b = (q - zero_point) * V[n, k / group_k], V fp16 */
+  QG_QUANT_BLOCK_F32 = 2  /* e4m3 A or B: value = code * scale of its (group_mn x group_k) block */
+} qg_quant_kind;
+
+typedef struct qg_quant {
+  int32_t kind;      /* qg_quant_kind */
+  int32_t group_k;   /* K extent of a scale group (128 for the kernels here) */
+  int32_t group_mn;  /* M (for A) or N (for B) extent of a scale block; 1 = per row */
+  int32_t zero_point;
+} qg_quant;
+
+typedef enum qg_schedule {
+  QG_SCHED_AUTO = 0,
+  QG_SCHED_DP = 1,       /* one workgroup per output tile, whole K */
+  QG_SCHED_SPLITK = 2,   /* each tile's K cut into split_k contiguous chunks */
+  QG_SCHED_STREAMK = 3   /* `programs` workgroups share the k-iterations evenly */
+} qg_schedule;
+
+typedef struct qg_operation {
+  int32_t policy;    /* qg_policy */
+  int32_t epilogue;  /* qg_epilogue */
+  qg_quant quant_a;
+  qg_quant quant_b;
+  int32_t schedule;  /* qg_schedule (honoured under FORCE; a hint otherwise) */
+  int32_t split_k;   /* SPLITK chunk count, 0 = engine's choice */
+  int32_t programs;  /* STREAMK program count, 0 = number of compute units */
+  int32_t kernel;    /* FORCE: registry index from qg_kernel_name, -1 = engine's choice */
+} qg_operation;
+
+/* Caller-owned workspace. `barriers` holds one int32 arrival counter per
+ * output tile of a split run; it must be zeroed once by the caller before
+ * first use, and every run leaves it zeroed again. `partials` holds fp32
+ * (int32 for int8) partial tiles of split-K / stream-K segments. */
+typedef struct qg_workspace {
+  void* barriers;
+  size_t barriers_size;
+  void* partials;
+  size_t partials_size;
+} qg_workspace;
+
+/* ---- lifetime ------------------------------------------------------------ */
+/* Creates a handle bound to the HIP device current on the calling thread
+ * ("created once per model/device"). It owns the kernel registry and the
+ * dispatch cache; it holds no device memory. */
+int qg_create(qg_handle** out);
+int qg_destroy(qg_handle* h);
+
+/* Workspace sizes the engine is built for (kBarriersSize, kPartialsSize of
+ * the Gemm class): 1 MiB and 32 MiB. */
+size_t qg_barriers_size(void);
+size_t qg_partials_size(void);
+
+/* ---- the GEMM ------------------------------------------------------------ */
+/* Operand order and meaning follow Gemm::Run. U, V and C may be NULL when
+ * unused (C only when beta == 0: then C is never read, so NaNs in it do not
+ * propagate). alpha == 0 still reads A and B. Supported combinations:
+ *   A, B bf16 | fp16            -> D f32 | bf16 | fp16, C f32 | bf16 | fp16
+ *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128)
+ *   A, B e4m3 + U, V fp32 (QG_QUANT_BLOCK_F32 on both; A 1 x 128, B 128 x 128)
+ *   A, B int8 -> D int32, C int32; alpha must be 1 and beta 0 or 1 (exact)
+ *   any of these grouped over experts (Adesc.num = Bdesc.num = E, offsets).
+ * Returns QG_ERR_* without launching on any invalid or unsupported request. */
+int qg_run(qg_handle* h, const qg_operation* op, float alpha,
+           const void* A, const qg_layout* Adesc,
+           const void* U, const qg_layout* Udesc,
+           const void* B, const qg_layout* Bdesc,
+           const void* V, const qg_layout* Vdesc,
+           float beta,
+           const void* C, const qg_layout* Cdesc,
+           void* D, const qg_layout* Ddesc,
+           const qg_workspace* ws, hipStream_t stream);
+
+/* What qg_run would launch for these arguments, without launching (no
+ * device access, no measuring). `desc` receives a NUL-terminated text line
+ * "kernel=<name> schedule=<dp|splitk|streamk> split=<s> programs=<p>
+ * tiles=<t> grid=<g> partials=<bytes> barriers=<bytes>"; `cap` is its size. */
+int qg_plan(qg_handle* h, const qg_operation* op,
+            const qg_layout* Adesc, const qg_layout* Udesc,
+            const qg_layout* Bdesc, const qg_layout* Vdesc,
+            const qg_layout* Cdesc, const qg_layout* Ddesc,
+            float alpha, float beta, const qg_workspace* ws,
+            char* desc, size_t cap);
+
+/* ---- dispatch cache ("Export/Import", "GetTuningSeq") ---------------------- */
+/* Serialises the dispatch cache as versioned text. With buf == NULL (or cap
+ * too small) *len receives the size needed (including the final NUL) and the
+ * call returns 0 (NULL buf) or QG_ERR_BUFFER_SMALL. */
+int qg_export(qg_handle* h, char* buf, size_t cap, size_t* len);
+/* Merges cache text produced by qg_export. All-or-nothing: on any error
+ * (QG_ERR_FORMAT) the cache is left unchanged. Entries for another GPU
+ * architecture are rejected with QG_ERR_FORMAT. */
+int qg_import(qg_handle* h, const char* buf, size_t len);
+/* Batch-size (M) tuning sequence: writes min(cap, total) values, *count = total. */
+int qg_get_tuning_seq(qg_handle* h, int* out, int cap, int* count);
+/* Number of cache entries (for tests and tools). */
+int qg_cache_size(qg_handle* h, int* count);
+
+/* ---- registry introspection --------------------------------------------- */
+int qg_kernel_count(void);
+/* Name of registry entry `index`, or NULL when out of range. */
+const char* qg_kernel_name(int index);
+
+/* Static text for a status code. */
+const char* qg_status_str(int status);
+/* Library version string. */
+const char* qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

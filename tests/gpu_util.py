@@ -1,0 +1,130 @@
+"""Helpers for GPU parity tests: upload seeded inputs, call the engine through
+the C ABI binding, read results back, compare with the fp64 oracle."""
+import numpy as np
+import torch
+
+import oracle
+import quantized_gemm_bf16_amd as qg
+from tests import tolerance
+
+_TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i32": torch.int32}
+
+
+def dev(arr):
+    """numpy array (any bit pattern) -> contiguous device tensor holding the same bytes."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to("cuda")
+
+
+def host_f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy() if t.dtype != torch.int32 else t.cpu().numpy().astype(np.float64)
+
+
+def decode_c(p):
+    if p.get("C") is None:
+        return None
+    c = p["C"]
+    if p["c_dtype"] == "bf16":
+        return torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).double().numpy()
+    if p["c_dtype"] == "f16":
+        return c.view(np.float16).astype(np.float64)
+    return c.astype(np.float64)
+
+
+class Run:
+    """Uploads a problem once; `run(op)` launches and returns D on the host."""
+
+    def __init__(self, gemm, p, ws=None, out_dtype=None):
+        self.g, self.p = gemm, p
+        self.ws = ws
+        self.out = out_dtype or p["out_dtype"]
+        M, N, K = p["M"], p["N"], p["K"]
+        self.A = dev(p["A"])
+        self.B = dev(p["B"])
+        # C and D rows are padded to a multiple of 8 elements (16-byte row pitch)
+        self.ldn = -(-N // 8) * 8
+        self.C = None
+        if p.get("C") is not None:
+            cp = np.zeros((M, self.ldn), dtype=p["C"].dtype)
+            cp[:, :N] = p["C"]
+            self.C = dev(cp)
+        self.U = dev(p["U"]) if p.get("U") is not None else None
+        self.V = dev(p["V"]) if p.get("V") is not None else None
+        self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") if self.out != "i32" \
+            else torch.full((M, self.ldn), -7, dtype=torch.int32, device="cuda")
+        kind = p["kind"]
+        if kind == "grouped":
+            E = p["E"]
+            self.off = dev(np.asarray(p["offsets"], dtype=np.int32))
+            self.Ad = qg.layout(p["in_dtype"], M, K, num=E, offsets=self.off.data_ptr())
+            self.Bd = qg.layout(p["in_dtype"], N, K, num=E, stride=N * K)
+            self.Dd = qg.layout(self.out, M, N, ld=self.ldn, num=E, offsets=self.off.data_ptr())
+        else:
+            bt = "u4" if kind == "w4a16" else p["in_dtype"]
+            self.Ad = qg.layout(p["in_dtype"], M, K)
+            self.Bd = qg.layout(bt, N, K)
+            self.Dd = qg.layout(self.out, M, N, ld=self.ldn)
+        self.Cd = qg.layout(p["c_dtype"], M, N, ld=self.ldn) if self.C is not None else None
+        self.Ud = self.Vd = None
+        if kind == "w4a16":
+            self.Vd = qg.layout("f16", N, p["V"].shape[1])
+        if p.get("U") is not None and kind == "grouped":
+            self.Ud = qg.layout("f32", M, p["U"].shape[1], num=p["E"], offsets=self.off.data_ptr())
+            self.Vd = qg.layout("f32", p["V"].shape[1], p["V"].shape[2], num=p["E"], stride=p["V"].shape[1] * p["V"].shape[2])
+
+    def op(self, **kw):
+        if self.p["kind"] == "w4a16":
+            kw.setdefault("quant_b", (qg.QUANT_INT4_ZP, self.p["group"], 1, self.p["zero_point"]))
+        if self.p["kind"] == "grouped" and self.p["in_dtype"] == "e4m3":
+            kw.setdefault("quant_a", (qg.QUANT_BLOCK_F32, self.p["group_k"], 1, 0))
+            kw.setdefault("quant_b", (qg.QUANT_BLOCK_F32, self.p["group_k"], self.p["group_n"], 0))
+        return qg.operation(**kw)
+
+    def launch(self, op=None, alpha=None, beta=None):
+        p = self.p
+        op = op or self.op()
+        st = self.g.run_raw(op, p["alpha"] if alpha is None else alpha, self.A, self.Ad, self.U, self.Ud, self.B,
+                            self.Bd, self.V, self.Vd, p["beta"] if beta is None else beta, self.C, self.Cd, self.D,
+                            self.Dd, self.ws.desc if self.ws is not None else None)
+        return st
+
+    def run(self, op=None, **kw):
+        st = self.launch(op, **kw)
+        if st != qg.OK:
+            raise qg.QGemmError(st, "qg_run")
+        torch.cuda.synchronize()
+        D = host_f64(self.D)
+        pad = D[:, self.p["N"]:]
+        if self.out == "i32":
+            assert (pad == -7).all(), "write past column N"
+        else:
+            assert np.isnan(pad).all(), "write past column N"
+        return np.ascontiguousarray(D[:, :self.p["N"]])
+
+    def plan(self, op=None):
+        p = self.p
+        return self.g.plan(op or self.op(), self.Ad, self.Ud, self.Bd, self.Vd, self.Cd, self.Dd, p["alpha"], p["beta"],
+                           self.ws.desc if self.ws is not None else None)
+
+
+def check_against_oracle(p, D, rows=None, what=""):
+    """Float paths: the tolerance rule; int8 -> int32: exact."""
+    ref, absdot = oracle.gemm(p, rows=rows)
+    Dsel = D if rows is None else D[np.asarray(rows)]
+    if p["out_dtype"] == "i32":
+        assert np.array_equal(Dsel, ref), f"{what}: int32 result differs from the exact sum"
+        return 0.0
+    c = decode_c(p)
+    if c is not None and rows is not None:
+        c = c[np.asarray(rows)]
+    return tolerance.check(Dsel, ref, absdot, p["alpha"], p["beta"], c, p["out_dtype"], what)
+
+
+def sample_rows(M, n, seed=1234):
+    g = np.random.default_rng(seed)
+    rows = {0, M - 1} | set(g.integers(0, M, size=n).tolist())
+    return sorted(rows)

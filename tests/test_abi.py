@@ -1,0 +1,212 @@
+"""CPU tests of libqgemm.so's C ABI: exported symbols, argument validation,
+planning, the dispatch cache's export/import and the tuning sequence.
+
+No call here reaches a kernel launch: every qg_run request is rejected during
+validation (fake device addresses are never dereferenced), and plans come from
+qg_plan, which never touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_bf16_amd as qg
+from oracle import streamk_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qg_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(qg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(qg.EXPORTS)
+
+
+def test_constants_and_strings():
+    assert qg.barriers_size() == 1 << 20
+    assert qg.partials_size() == 32 << 20
+    assert qg.version().startswith("qgemm")
+    assert qg.status_str(0) == "ok"
+    assert "workspace" in qg.status_str(qg.ERR_WORKSPACE)
+    names = qg.kernel_names()
+    assert len(names) == qg.lib.qg_kernel_count() and len(set(names)) == len(names)
+    assert qg.lib.qg_kernel_name(-1) is None and qg.lib.qg_kernel_name(len(names)) is None
+
+
+@pytest.fixture(scope="module")
+def g():
+    return qg.Gemm()
+
+
+def ws_desc(b=1 << 20, p=32 << 20):
+    return qg.Workspace(FAKE, b, FAKE, p)
+
+
+def dense(M, N, K, t="bf16", out="bf16"):
+    return qg.layout(t, M, K), qg.layout(t, N, K), qg.layout(out, M, N)
+
+
+def run(g, op=None, alpha=1.0, A=FAKE, Ad=None, B=FAKE, Bd=None, beta=0.0, C=None, Cd=None, D=FAKE, Dd=None,
+        U=None, Ud=None, V=None, Vd=None, ws=None):
+    return g.run_raw(op or qg.operation(), alpha, A, Ad, U, Ud, B, Bd, V, Vd, beta, C, Cd, D, Dd, ws, stream=None)
+
+
+def test_invalid_arguments(g):
+    Ad, Bd, Dd = dense(64, 64, 64)
+    assert run(g, Ad=None, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, A=None) == qg.ERR_INVALID_ARG
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, D=None) == qg.ERR_INVALID_ARG
+    # shape mismatch
+    assert run(g, Ad=Ad, Bd=qg.layout("bf16", 64, 32), Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, Ad=Ad, Bd=Bd, Dd=qg.layout("bf16", 64, 65)) == qg.ERR_INVALID_ARG
+    # ld smaller than the row
+    assert run(g, Ad=qg.layout("bf16", 64, 64, ld=32), Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    # beta != 0 without C
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, beta=1.0) == qg.ERR_INVALID_ARG
+    # non-finite scalars
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, alpha=float("nan")) == qg.ERR_INVALID_ARG
+    # a bad policy
+    assert run(g, op=qg.operation(policy=9), Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert qg.lib.qg_run(None, None, 1.0, None, None, None, None, None, None, None, None, 0.0, None, None, None,
+                         None, None, None) == qg.ERR_INVALID_ARG
+
+
+def test_alignment(g):
+    Ad, Bd, Dd = dense(64, 64, 64)
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, A=FAKE + 2) == qg.ERR_ALIGNMENT
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, D=FAKE + 8) == qg.ERR_ALIGNMENT
+    # rows not a multiple of 16 bytes
+    assert run(g, Ad=qg.layout("bf16", 64, 60), Bd=qg.layout("bf16", 64, 60), Dd=Dd) == qg.ERR_ALIGNMENT
+    assert run(g, Ad=qg.layout("bf16", 64, 64, ld=68), Bd=Bd, Dd=Dd) == qg.ERR_ALIGNMENT
+
+
+def test_unsupported(g):
+    Ad, Bd, Dd = dense(64, 64, 64)
+    assert run(g, Ad=qg.layout("bf16", 64, 64, order=qg.COL_MAJOR), Bd=Bd, Dd=Dd) == qg.ERR_UNSUPPORTED
+    assert run(g, Ad=Ad, Bd=qg.layout("f16", 64, 64), Dd=Dd) == qg.ERR_UNSUPPORTED
+    assert run(g, Ad=Ad, Bd=Bd, Dd=qg.layout("i32", 64, 64)) == qg.ERR_UNSUPPORTED
+    i8 = dense(64, 64, 64, "i8", "i32")
+    assert run(g, Ad=i8[0], Bd=i8[1], Dd=i8[2], alpha=2.0) == qg.ERR_UNSUPPORTED
+    Cd = qg.layout("i32", 64, 64)
+    assert run(g, Ad=i8[0], Bd=i8[1], Dd=i8[2], beta=0.5, C=FAKE, Cd=Cd) == qg.ERR_UNSUPPORTED
+    assert run(g, Ad=i8[0], Bd=i8[1], Dd=qg.layout("f32", 64, 64)) == qg.ERR_UNSUPPORTED
+    assert run(g, op=qg.operation(quant_a=(qg.QUANT_INT4_ZP, 128, 1, 8)), Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_UNSUPPORTED
+
+
+def test_workspace_checks(g):
+    Ad, Bd, Dd = dense(16, 4096, 14336)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    assert run(g, op=op, Ad=Ad, Bd=Bd, Dd=Dd, ws=None) == qg.ERR_WORKSPACE
+    assert run(g, op=op, Ad=Ad, Bd=Bd, Dd=Dd, ws=ws_desc(p=1024)) == qg.ERR_WORKSPACE
+    assert run(g, op=op, Ad=Ad, Bd=Bd, Dd=Dd, ws=ws_desc(b=16)) == qg.ERR_WORKSPACE
+    # DEFAULT policy without a workspace falls back to a data-parallel plan
+    desc = g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, None)
+    assert "schedule=dp" in desc
+
+
+def test_plan_decode_split8(g):
+    Ad, Bd, Dd = dense(16, 4096, 14336)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    d = dict(kv.split("=") for kv in g.plan(op, Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["schedule"] == "splitk" and d["split"] == "8"
+    assert int(d["grid"]) == int(d["tiles"]) * 8
+    assert int(d["partials"]) <= 32 << 20 and int(d["barriers"]) <= 1 << 20
+
+
+def test_plan_streamk_matches_planner(g):
+    M, N, K = 16, 4096, 14336
+    Ad, Bd, Dd = dense(M, N, K)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=256)
+    d = dict(kv.split("=") for kv in g.plan(op, Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["schedule"] == "streamk" and d["programs"] == "256" and d["grid"] == "256"
+    name = d["kernel"]
+    bm, bn = map(int, re.search(r"_(\d+)x(\d+)_", name).groups())
+    pl = streamk_plan(M, N, K, bm, bn, 64, 256)
+    assert int(d["tiles"]) == pl["total_tiles"]
+    assert int(d["partials"]) == 2 * 256 * bm * bn * 4
+
+
+def test_plan_square_uses_one_wave_of_big_tiles(g):
+    Ad, Bd, Dd = dense(4096, 4096, 4096)
+    d = dict(kv.split("=") for kv in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["schedule"] == "dp" and d["kernel"].startswith("tile_BF16_256x256")
+    assert d["tiles"] == "256"
+
+
+def test_plan_zero_sized(g):
+    Ad, Bd, Dd = dense(0, 64, 64)
+    assert "grid=0" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, None)
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd) == qg.OK  # nothing to do, nothing launched
+
+
+def test_tuning_sequence(g):
+    seq = g.tuning_seq()
+    assert seq[0] == 1 and seq == sorted(seq) and 16 in seq and 4096 in seq and len(seq) == len(set(seq))
+
+
+CACHE = """qgemm-cache 1 arch=gfx950 entries=2
+16|bf16.bf16.-.bf16.q00.e0.n4096.k14336 kernel=tile_BF16_32x64_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
+4096|bf16.bf16.-.bf16.q00.e0.n4096.k4096 kernel=tile_BF16_128x128_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
+"""
+
+
+def test_cache_import_export_roundtrip_and_lookup():
+    g = qg.Gemm()
+    assert g.cache_size() == 0
+    assert g.import_(CACHE) == qg.OK
+    assert g.cache_size() == 2
+    out = g.export()
+    assert out.splitlines()[0] == "qgemm-cache 1 arch=gfx950 entries=2"
+    assert sorted(out.splitlines()[1:]) == sorted(CACHE.splitlines()[1:])
+    g2 = qg.Gemm()
+    assert g2.import_(out) == qg.OK and g2.export() == out
+    # the DEFAULT policy uses the cached choice, also for an M that maps to the same bucket
+    Ad, Bd, Dd = dense(16, 4096, 14336)
+    assert "kernel=tile_BF16_32x64_w1x2_s6 schedule=splitk split=4" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    Ad, Bd, Dd = dense(11, 4096, 14336)
+    assert "kernel=tile_BF16_32x64_w1x2_s6" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    # REUSE misses where nothing is cached
+    Ad, Bd, Dd = dense(16, 2048, 2048)
+    with pytest.raises(qg.QGemmError) as e:
+        g.plan(qg.operation(policy=qg.POLICY_REUSE), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    assert e.value.status == qg.ERR_NO_KERNEL
+
+
+@pytest.mark.parametrize("bad", [
+    "",
+    "nonsense\n",
+    "qgemm-cache 2 arch=gfx950 entries=0\n",
+    "qgemm-cache 1 arch=gfx942 entries=0\n",
+    CACHE.replace("entries=2", "entries=3"),
+    CACHE.replace("kernel=tile_BF16_32x64_w1x2_s6", "kernel=no_such_kernel"),
+    CACHE.replace("schedule=dp", "schedule=zigzag"),
+    CACHE.replace("split=4", "split=x"),
+    CACHE.replace("us=90.000", "us=90.000 extra"),
+    CACHE[: len(CACHE) // 2],
+])
+def test_cache_import_is_all_or_nothing(bad):
+    g = qg.Gemm()
+    assert g.import_(CACHE) == qg.OK
+    before = g.export()
+    assert g.import_(bad) == qg.ERR_FORMAT
+    assert g.export() == before
+
+
+def test_export_buffer_too_small():
+    g = qg.Gemm()
+    assert g.import_(CACHE) == qg.OK
+    n = ctypes.c_size_t()
+    assert qg.lib.qg_export(g.h, None, 0, ctypes.byref(n)) == qg.OK
+    buf = ctypes.create_string_buffer(4)
+    assert qg.lib.qg_export(g.h, buf, 4, ctypes.byref(n)) == qg.ERR_BUFFER_SMALL
+    assert n.value == len(g.export()) + 1

@@ -1,0 +1,164 @@
+"""GPU parity of the dense paths (bf16 / fp16 / int8) against the fp64 oracle,
+called through the C ABI. Sizes span several tiles with ragged tails; the
+full-size workloads are checked on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_bf16_amd as qg
+import synth
+from tests.gpu_util import Run, check_against_oracle, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return qg.Gemm()
+
+
+@pytest.fixture(scope="module")
+def ws():
+    return qg.workspace()
+
+
+def kidx(name):
+    return qg.kernel_names().index(name)
+
+
+def test_tiny_config(g, ws):
+    p = synth.config_tiny()
+    r = Run(g, p, ws)
+    print("plan:", r.plan(), flush=True)
+    D = r.run()
+    check_against_oracle(p, D, what="256^3 bf16 alpha 1.5 beta 0.5 fp32 out")
+
+
+@pytest.mark.parametrize("kname", ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4",
+                                   "tile_BF16_32x128_w1x4_s4", "tile_BF16_32x64_w1x2_s6"])
+@pytest.mark.parametrize("shape", [(300, 200, 136), (257, 513, 264), (64, 64, 64), (33, 1000, 72), (1, 130, 8)])
+def test_ragged_each_kernel(g, ws, kname, shape):
+    M, N, K = shape
+    p = synth.dense_problem(M, N, K, "bf16", "bf16", c_dtype="f32", alpha=0.75, beta=-1.25, dist="uniform", seed=M + N + K)
+    r = Run(g, p, ws)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+    print(kname, shape, r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"{kname} {shape}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("cdt", [None, "f32", "bf16", "f16"])
+def test_output_and_c_types(g, ws, out, cdt):
+    p = synth.dense_problem(96, 80, 192, "bf16", out, c_dtype=cdt, alpha=1.0, beta=0.5 if cdt else 0.0, dist="uniform", seed=7)
+    check_against_oracle(p, Run(g, p, ws).run(), what=f"out {out} C {cdt}")
+
+
+@pytest.mark.parametrize("nk", [1, 2, 3, 5, 7, 8])
+def test_odd_and_even_k_tile_counts(g, ws, nk):
+    # 64 bf16 per k-tile: an odd k-tile count changes which ring stage the last tile uses
+    p = synth.dense_problem(256, 256, 64 * nk, "bf16", "f32", dist="normal", seed=nk)
+    for kname in ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4", "tile_BF16_32x64_w1x2_s6"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+        check_against_oracle(p, Run(g, p, ws).run(op), what=f"{kname} k-tiles {nk}")
+
+
+def test_fp16_ragged(g, ws):
+    p = synth.dense_problem(200, 328, 456, "f16", "f16", c_dtype="f16", alpha=1.0, beta=1.0, dist="uniform", seed=9)
+    for kname in ["tile_F16_256x256_w2x4_s2", "tile_F16_128x128_w2x2_s4", "tile_F16_32x128_w1x4_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+        check_against_oracle(p, Run(g, p, ws).run(op), what=kname)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 8])
+def test_splitk_matches_oracle_and_leaves_barriers_zero(g, ws, split):
+    p = synth.dense_problem(48, 520, 2056, "bf16", "bf16", c_dtype="bf16", alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02, seed=11)
+    r = Run(g, p, ws)
+    for kname in ["tile_BF16_32x128_w1x4_s4", "tile_BF16_128x128_w2x2_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=split, kernel=kidx(kname))
+        print(kname, r.plan(op), flush=True)
+        D1 = r.run(op)
+        check_against_oracle(p, D1, what=f"{kname} split {split}")
+        assert int(ws.barriers.abs().sum().item()) == 0
+        D2 = r.run(op)
+        assert np.array_equal(D1, D2), "split-K result must not depend on arrival order"
+
+
+@pytest.mark.parametrize("programs", [256, 7, 100])
+def test_streamk(g, ws, programs):
+    p = synth.dense_problem(200, 700, 1000, "bf16", "f32", c_dtype="f32", alpha=1.0, beta=0.5, dist="uniform", seed=13)
+    r = Run(g, p, ws)
+    for kname in ["tile_BF16_128x128_w2x2_s4", "tile_BF16_32x128_w1x4_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=programs, kernel=kidx(kname))
+        print(kname, r.plan(op), flush=True)
+        D1 = r.run(op)
+        check_against_oracle(p, D1, what=f"{kname} stream-K {programs}")
+        assert int(ws.barriers.abs().sum().item()) == 0
+        assert np.array_equal(D1, r.run(op))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("sched", ["splitk8", "streamk"])
+def test_decode_config_full_size(g, ws, M, sched):
+    p = synth.config_decode(M=M)
+    r = Run(g, p, ws)
+    if sched == "splitk8":
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    else:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=256)
+    print(r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"decode M={M} {sched}")
+    assert int(ws.barriers.abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_square_4096_sampled_rows(g, ws, dtype):
+    p = synth.config_square(dtype)
+    r = Run(g, p, ws)
+    print(r.plan(), flush=True)
+    D = r.run()
+    rows = sample_rows(4096, 24)
+    check_against_oracle(p, D, rows=rows, what=f"4096^3 {dtype}")
+
+
+# ---------------------------------------------------------------- int8 -> int32, bit-exact
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 200, 144), (1, 77, 528)])
+def test_int8_exact(g, ws, shape):
+    M, N, K = shape
+    p = synth.dense_problem(M, N, K, "i8", "i32", c_dtype="i32", alpha=1.0, beta=1.0, seed=M * 3 + K)
+    r = Run(g, p, ws)
+    for kname in ["tile_I8_256x256_w2x4_s2", "tile_I8_128x128_w2x2_s4", "tile_I8_32x128_w1x4_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+        check_against_oracle(p, r.run(op), what=f"{kname} {shape}")
+
+
+def test_int8_decode_split8_exact(g, ws):
+    p = synth.dense_problem(16, 4096, 14336, "i8", "i32", c_dtype=None, alpha=1.0, beta=0.0, seed=5)
+    r = Run(g, p, ws)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    check_against_oracle(p, r.run(op), what="int8 decode split 8")
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=256)
+    check_against_oracle(p, r.run(op), what="int8 decode stream-K")
+
+
+def test_int8_square_4096_sampled(g, ws):
+    p = synth.dense_problem(4096, 4096, 4096, "i8", "i32", seed=3)
+    D = Run(g, p, ws).run()
+    check_against_oracle(p, D, rows=sample_rows(4096, 8), what="int8 4096^3")
+
+
+# ---------------------------------------------------------------- grouped
+def test_grouped_small_with_empty_experts(g, ws):
+    counts = np.array([5, 0, 300, 1, 0, 129, 256, 0], dtype=np.int32)
+    p = synth.grouped_problem(counts, 384, 256, seed=17)
+    r = Run(g, p, ws)
+    for kname in ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, kernel=kidx(kname))
+        print(kname, r.plan(op), flush=True)
+        check_against_oracle(p, r.run(op), what=f"grouped {kname}")
+
+
+def test_tiny_config_plan_is_logged(g, ws):
+    p = synth.config_tiny()
+    desc = Run(g, p, ws).plan()
+    assert desc.startswith("kernel=tile_BF16_")
