@@ -188,8 +188,9 @@ int qg_run(qg_handle* h, const qg_operation* op, float alpha,
 
 /* What qg_run would launch for these arguments, without launching (no
  * device access, no measuring). `desc` receives a NUL-terminated text line
- * "kernel=<name> schedule=<dp|splitk|streamk> split=<s> programs=<p>
- * tiles=<t> grid=<g> partials=<bytes> barriers=<bytes>"; `cap` is its size. */
+ * "kernel=<name> schedule=<dp|splitk|streamk|grouped> split=<s> programs=<p>
+ * tiles=<t> grid=<g> partials=<bytes> barriers=<bytes> bm=<rows> bn=<cols>
+ * bk=<k per iteration>"; `cap` is its size. */
 int qg_plan(qg_handle* h, const qg_operation* op,
             const qg_layout* Adesc, const qg_layout* Udesc,
             const qg_layout* Bdesc, const qg_layout* Vdesc,

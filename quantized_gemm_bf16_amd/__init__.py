@@ -63,10 +63,10 @@ class QGemmError(RuntimeError):
         super().__init__(f"{what}: {status_str(status)} ({status})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_gemm_bf16_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m quantized_gemm_bf16_amd.build`")
+    L = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     P = ctypes.POINTER
     L.qg_create.argtypes = [P(vp)]

@@ -14,6 +14,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -32,13 +33,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Offset that is always outside a resource (resources are < 2^31 bytes here).
 constexpr uint32_t kOOB = 0x80000000u;
 
-// One 16-byte chunk per lane, written to LDS at lds_wave_base + 16 * lane.
-__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voff, 0, 0, 0);
+// 128-bit buffer descriptor as four dwords (gfx9 layout: base address,
+// stride 0, num_records, dword3 flags), for use in inline assembly.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (int)(__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xFFFF),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// One 16-byte chunk per lane, written to LDS at lds_wave_base + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the wave's LDS base). Issued from
+// inline assembly on purpose: the compiler cannot tell which part of LDS an
+// in-flight direct load writes, so for loads it knows about it waits for all
+// of them (vmcnt 0) before every LDS read, draining a multi-stage ring. The
+// callers wait for exactly the loads they need with wait_vmcnt<N>() instead.
+__device__ __forceinline__ void load_lds_x4(const i32x4& rsrc, void* lds_wave_base, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
 }
 // One dword per lane, written to LDS at lds_wave_base + 4 * lane.
 __device__ __forceinline__ void load_lds_x1(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, voff, 0, 0, 0);
+}
+
+// 16-byte buffer store / load with the sc1 cache-policy bit (coherent at agent
+// scope across the XCDs' L2s; gfx950 cache-policy encoding: sc0 = 1, nt = 2,
+// sc1 = 16).
+__device__ __forceinline__ void store_sc1_x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, i32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 16);
+}
+__device__ __forceinline__ i32x4 load_sc1_x4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 16));
+}
+
+// Plain 16-byte buffer load into registers (zero outside the resource).
+__device__ __forceinline__ i32x4 load_x4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -48,6 +84,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS ring. __syncthreads() carries a workgroup
+// release fence, which the compiler implements as a wait for ALL outstanding
+// vector-memory operations -- that would drain every prefetched stage. Here
+// the caller has already waited for exactly the loads it needs (wait_vmcnt);
+// this waits for the wave's own LDS reads (lgkmcnt 0) and meets the other
+// waves. The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---- MFMA (32x32 output tile per instruction) ------------------------------

@@ -229,7 +229,8 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
 
 // ---- registry filtering ("Context") ------------------------------------------
 bool compatible(const KernelInfo& k, const Problem& p) {
-  if (k.family != FAM_TILE) return false;
+  if (k.family != FAM_TILE && k.family != FAM_SKINNY) return false;
+  if (k.family == FAM_SKINNY && p.M > k.bm && p.E == 0) return false;  // skinny tiles cover all rows
   return k.in_type == p.ta && p.tb == p.ta;
 }
 
@@ -351,8 +352,34 @@ int kernel_by_shape(const Problem& p, int bm, int bn) {
   return -1;
 }
 
-// Shape heuristic used on a cache miss.
-Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws) {
+// Skinny kernel (M <= its row tile) for a target column-tile width: the
+// smallest registered width >= target (the widest if none is that wide);
+// among equal widths the one with the smallest row tile that covers M.
+int skinny_for(const Problem& p, int64_t target_bn) {
+  int best = -1;
+  for (int i = 0; i < kNumKernels; ++i) {
+    const KernelInfo& k = kKernels[i];
+    if (k.family != FAM_SKINNY || !compatible(k, p)) continue;
+    if (best < 0) {
+      best = i;
+      continue;
+    }
+    const KernelInfo& b = kKernels[best];
+    const bool k_ok = k.bn >= target_bn, b_ok = b.bn >= target_bn;
+    if (k_ok != b_ok) {
+      if (k_ok) best = i;
+      continue;
+    }
+    const bool better_bn = k_ok ? k.bn < b.bn : k.bn > b.bn;
+    if (better_bn || (k.bn == b.bn && k.bm < b.bm)) best = i;
+  }
+  return best;
+}
+
+// Shape heuristic used on a cache miss. `mode` / `split` are the schedule the
+// caller forces (MODE_DP with split 0 = nothing forced).
+Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, int forced_mode = -1,
+                 int forced_split = 0) {
   Choice c;
   const int cus = h->cus;
   if (p.E > 0) {
@@ -362,9 +389,28 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws) {
     c.mode = MODE_GROUPED;
     return c;
   }
+  const bool ws_ok = ws && ws->partials && ws->barriers;
   if (p.M <= 32) {
+    // Skinny GEMM: aim for about one workgroup per compute unit.
+    int64_t target = cdiv(p.N, cus);
+    if (forced_mode == MODE_SPLITK && forced_split > 1) target = cdiv(p.N * forced_split, cus);
+    // stream-K: fewer tiles than programs, so that tiles really are shared
+    if (forced_mode == MODE_STREAMK) target = cdiv(p.N * 2, cus);
+    c.kernel = skinny_for(p, target);
+    if (c.kernel >= 0) {
+      const KernelInfo& k = kKernels[c.kernel];
+      const int64_t tiles = cdiv(p.N, k.bn), iters = cdiv(p.K, k.bk);
+      c.mode = MODE_DP;
+      if (forced_mode < 0 && tiles < cus && iters >= 8 && ws_ok) {
+        const int s = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(cus, tiles), iters / 4));
+        if (s > 1 && (size_t)tiles * s * k.slot_bytes <= ws->partials_size && (size_t)tiles * 4 <= ws->barriers_size) {
+          c.mode = MODE_SPLITK;
+          c.split = s;
+        }
+      }
+      return c;
+    }
     c.kernel = kernel_by_shape(p, 32, 128);
-    if (c.kernel < 0) c.kernel = kernel_by_shape(p, 32, 64);
   } else if (p.M >= 2048 && p.N >= 2048) {
     c.kernel = kernel_by_shape(p, 256, 256);
   } else {
@@ -372,7 +418,7 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws) {
   }
   if (c.kernel < 0) {
     for (int i = 0; i < kNumKernels; ++i)
-      if (compatible(kKernels[i], p)) {
+      if (compatible(kKernels[i], p) && kKernels[i].family == FAM_TILE) {
         c.kernel = i;
         break;
       }
@@ -382,10 +428,10 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws) {
   const int64_t tiles = cdiv(p.M, k.bm) * cdiv(p.N, k.bn);
   const int64_t iters = cdiv(p.K, k.bk);
   c.mode = MODE_DP;
-  if (tiles < cus && iters >= 16) {
+  if (forced_mode < 0 && tiles < cus && iters >= 16) {
     int s = (int)std::min<int64_t>(cdiv(cus, tiles), iters / 8);
     s = std::max(1, std::min(s, 16));
-    if (s > 1 && ws && ws->partials && ws->barriers && (size_t)tiles * s * k.slot_bytes <= ws->partials_size &&
+    if (s > 1 && ws_ok && (size_t)tiles * s * k.slot_bytes <= ws->partials_size &&
         (size_t)tiles * 4 <= ws->barriers_size) {
       c.mode = MODE_SPLITK;
       c.split = s;
@@ -423,9 +469,11 @@ int launch(const Plan& pl, hipStream_t s) {
 
 std::string describe(const Plan& pl) {
   char buf[320];
-  snprintf(buf, sizeof buf, "kernel=%s schedule=%s split=%d programs=%d tiles=%d grid=%d partials=%zu barriers=%zu",
-           kKernels[pl.c.kernel].name, sched_name(pl.c.mode), pl.c.split, pl.c.programs, pl.tiles, pl.grid,
-           pl.partials, pl.barriers);
+  const KernelInfo& k = kKernels[pl.c.kernel];
+  snprintf(buf, sizeof buf,
+           "kernel=%s schedule=%s split=%d programs=%d tiles=%d grid=%d partials=%zu barriers=%zu bm=%d bn=%d bk=%d",
+           k.name, sched_name(pl.c.mode), pl.c.split, pl.c.programs, pl.tiles, pl.grid, pl.partials, pl.barriers, k.bm,
+           k.bn, k.bk);
   return std::string(buf);
 }
 
@@ -512,14 +560,14 @@ int resolve(qg_handle* h, const qg_operation* op, const Problem& p, const qg_wor
   Choice c;
   switch (op->policy) {
     case QG_POLICY_FORCE: {
-      c = heuristic(h, p, ws);
+      int fmode = -1;
+      if (op->schedule == QG_SCHED_DP) fmode = MODE_DP;
+      else if (op->schedule == QG_SCHED_SPLITK) fmode = MODE_SPLITK;
+      else if (op->schedule == QG_SCHED_STREAMK) fmode = MODE_STREAMK;
+      else if (op->schedule != QG_SCHED_AUTO) return QG_ERR_INVALID_ARG;
+      c = heuristic(h, p, ws, fmode, op->split_k);
       if (op->kernel >= 0) c.kernel = op->kernel;
-      if (op->schedule != QG_SCHED_AUTO) {
-        if (op->schedule == QG_SCHED_DP) c.mode = MODE_DP;
-        else if (op->schedule == QG_SCHED_SPLITK) c.mode = MODE_SPLITK;
-        else if (op->schedule == QG_SCHED_STREAMK) c.mode = MODE_STREAMK;
-        else return QG_ERR_INVALID_ARG;
-      }
+      if (fmode >= 0) c.mode = fmode;
       if (op->split_k > 0) c.split = op->split_k;
       if (c.mode == MODE_SPLITK && op->split_k <= 0 && c.split <= 1) c.split = 2;
       c.programs = op->programs;
@@ -626,7 +674,7 @@ int qg_plan(qg_handle* h, const qg_operation* op, const qg_layout* Adesc, const 
                     Vdesc, beta, Cdesc ? dummy : nullptr, Cdesc, const_cast<void*>(dummy), Ddesc, p);
   if (st != QG_OK) return st;
   if (p.M == 0 || p.N == 0) {
-    snprintf(desc, cap, "kernel=none schedule=none split=0 programs=0 tiles=0 grid=0 partials=0 barriers=0");
+    snprintf(desc, cap, "kernel=none schedule=none split=0 programs=0 tiles=0 grid=0 partials=0 barriers=0 bm=0 bn=0 bk=0");
     return QG_OK;
   }
   Plan pl;

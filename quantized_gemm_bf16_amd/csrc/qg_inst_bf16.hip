@@ -1,12 +1,18 @@
-// Explicit instantiations of the bf16 tile kernels listed in qg_kernel_list.inc.
-#include "qg_tile.hpp"
+// Explicit instantiations of the bf16 kernels listed in qg_kernel_list.inc.
+#include "qg_skinny.hpp"
 
 namespace qg {
-#define QG_TILE_BF16(BM, BN, WM, WN, ST)
-#define QG_TILE_F16(BM, BN, WM, WN, ST)
-#define QG_TILE_I8(BM, BN, WM, WN, ST)
+#define QG_TILE_BF16(BM, BN, WM, WN, ST, RB)
+#define QG_TILE_F16(BM, BN, WM, WN, ST, RB)
+#define QG_TILE_I8(BM, BN, WM, WN, ST, RB)
+#define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS)
+#define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS)
+#define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS)
 #undef QG_TILE_BF16
-#define QG_TILE_BF16(BM, BN, WM, WN, ST) \
-  template hipError_t launch_tile<TileCfg<El::BF16, BM, BN, WM, WN, ST>>(const Args&, int, hipStream_t);
+#undef QG_SKINNY_BF16
+#define QG_TILE_BF16(BM, BN, WM, WN, ST, RB) \
+  template hipError_t launch_tile<TileCfg<El::BF16, BM, BN, WM, WN, ST, RB>>(const Args&, int, hipStream_t);
+#define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) \
+  template hipError_t launch_skinny<SkinnyCfg<El::BF16, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"
 }  // namespace qg

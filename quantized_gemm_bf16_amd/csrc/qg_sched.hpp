@@ -1,0 +1,228 @@
+// Work division shared by every kernel core (DP, split-K, stream-K, grouped).
+//
+// A core supplies: BM, BN (output tile), NT (threads), SMEM_BYTES, an Acc
+// type holding one tile's accumulators, mainloop(a, unit, smem, acc) over the
+// unit's k-tiles, store(a, unit, acc) (epilogue), and write_partial /
+// add_partial on the partials workspace.
+//
+//   DP       one unit = one whole tile; with one workgroup per tile the block
+//            id is remapped so each XCD (own L2) gets a contiguous range.
+//   SPLITK   tile t, chunk s: k-tiles [s*ips, min(iters, (s+1)*ips)).
+//   STREAMK  program p takes the contiguous k-iterations
+//            [p*full + min(p, partial), (p+1)*full + min(p+1, partial)) of the
+//            stream-K tiles, cut at tile boundaries, then whole "blocking"
+//            tiles round-robin (TileLang tutorial "gemm_variants.py",
+//            gemm_streamk / streamk_plan; tile ids past the count skipped).
+//   GROUPED  persistent loop over the tiles of all experts, found from the
+//            device offsets array (tutorial function gemm_grouped: padded
+//            per-expert m-block prefix; rows past an expert's end masked).
+// Split segments write fp32/int32 partial tiles to the partials workspace and
+// bump the tile's arrival counter by their k-iteration count. The segment
+// that completes the count sums all segments of the tile in k order (so the
+// result does not depend on arrival order), applies the epilogue and zeroes
+// the counter. Nothing ever waits on another workgroup.
+#pragma once
+#include "qg_args.hpp"
+#include "qg_device.hpp"
+
+namespace qg {
+
+struct Unit {
+  int tile;         // counter / slot index
+  int m0, n0;       // first row of A/D, first row of B (= first column of D)
+  int m_end;        // rows [m0, m_end) valid
+  int expert;
+  int kb, ke;       // k-tile range [kb, ke)
+};
+
+template <class Core>
+struct Sched {
+  using Acc = typename Core::Acc;
+
+  // Tile coordinates of a non-grouped tile id (super-grouped along M).
+  __device__ __forceinline__ static void coords(const Args& a, int t, int& tm, int& tn) {
+    const int per = a.group_m * a.tiles_n;
+    const int g = t / per, first = g * a.group_m;
+    const int gm = min(a.tiles_m - first, a.group_m);
+    const int r = t - g * per;
+    tm = first + r % gm;
+    tn = r / gm;
+  }
+
+  __device__ __forceinline__ static Unit make_unit(const Args& a, int t, int kb, int ke) {
+    int tm, tn;
+    coords(a, t, tm, tn);
+    Unit u;
+    u.tile = t;
+    u.m0 = tm * Core::BM;
+    u.n0 = tn * Core::BN;
+    u.m_end = a.M;
+    u.expert = 0;
+    u.kb = kb;
+    u.ke = ke;
+    return u;
+  }
+
+  // Publishes a partial segment; returns true in the workgroup that completed
+  // the tile. Order: every lane's sc1 stores are acknowledged (vmcnt 0) before
+  // the workgroup barrier, the counter is bumped only after the barrier, and
+  // the completing workgroup reads partials only after the counter returned.
+  __device__ __forceinline__ static bool arrive(const Args& a, const Unit& u, int slot, Acc& acc, int* flag) {
+    Core::write_partial(a, slot, acc);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int nk = u.ke - u.kb;
+      const int old = __hip_atomic_fetch_add(a.counters + u.tile, nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = (old + nk == a.iters);
+    }
+    __syncthreads();
+    return *flag;
+  }
+
+  __device__ __forceinline__ static void finish_counter(const Args& a, const Unit& u) {
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + u.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- schedules ------------------------------------------------------------
+  __device__ __forceinline__ static int xcd_remap(int b, int G) {
+    // blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of ids
+    const int x = b & 7, q = G >> 3, r = G & 7;
+    return x * q + min(x, r) + (b >> 3);
+  }
+
+  __device__ __forceinline__ static void run_dp(const Args& a, char* smem) {
+    const int total = a.tiles_m * a.tiles_n;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int t = (gridDim.x == (unsigned)total) ? xcd_remap(b, total) : b;
+      Acc acc;
+      Unit u = make_unit(a, t, 0, a.iters);
+      Core::mainloop(a, u, smem, acc);
+      Core::store(a, u, acc);
+    }
+  }
+
+  __device__ __forceinline__ static void run_splitk(const Args& a, char* smem, int* flag) {
+    const int total = a.tiles_m * a.tiles_n * a.splits;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int t = b / a.splits, s = b % a.splits;
+      const int kb = s * a.iters_per_split, ke = min(a.iters, kb + a.iters_per_split);
+      Acc acc;
+      Unit u = make_unit(a, t, kb, ke);
+      Core::mainloop(a, u, smem, acc);
+      if (arrive(a, u, t * a.splits + s, acc, flag)) {
+        const int ns = (a.iters + a.iters_per_split - 1) / a.iters_per_split;
+        for (int q = 0; q < ns; ++q) Core::add_partial(a, t * a.splits + q, acc, q == 0);
+        Core::store(a, u, acc);
+        finish_counter(a, u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static int sk_start(const Args& a, int p) { return p * a.sk_full + min(p, a.sk_partial); }
+  __device__ __forceinline__ static int sk_owner(const Args& a, int it) {
+    const int big = a.sk_partial * (a.sk_full + 1);
+    return it < big ? it / (a.sk_full + 1) : a.sk_partial + (it - big) / a.sk_full;
+  }
+
+  __device__ __forceinline__ static void run_streamk(const Args& a, char* smem, int* flag) {
+    const int ipt = a.iters;
+    for (int pid = blockIdx.x; pid < a.programs; pid += gridDim.x) {
+      int it = sk_start(a, pid);
+      const int last = sk_start(a, pid + 1);
+      const int first_it = it;
+      while (it < last) {
+        const int t = it / ipt, rem = it - t * ipt;
+        const int end = min(it + (ipt - rem), last);
+        Acc acc;
+        Unit u = make_unit(a, t, rem, rem + (end - it));
+        Core::mainloop(a, u, smem, acc);
+        if (rem == 0 && end - it == ipt) {
+          Core::store(a, u, acc);
+        } else {
+          const int slot = 2 * pid + (it == first_it ? 0 : 1);
+          if (arrive(a, u, slot, acc, flag)) {
+            const int t0 = t * ipt;
+            const int plo = sk_owner(a, t0), phi = sk_owner(a, t0 + ipt - 1);
+            for (int q = plo; q <= phi; ++q) Core::add_partial(a, 2 * q + (sk_start(a, q) >= t0 ? 0 : 1), acc, q == plo);
+            Core::store(a, u, acc);
+            finish_counter(a, u);
+          }
+        }
+        it = end;
+      }
+      const int total = a.tiles_m * a.tiles_n;
+      for (int r = 0; r < a.dp_rounds; ++r) {
+        const int t = pid + a.sk_tiles + r * a.programs;
+        if (t >= total) break;
+        Acc acc;
+        Unit u = make_unit(a, t, 0, ipt);
+        Core::mainloop(a, u, smem, acc);
+        Core::store(a, u, acc);
+      }
+    }
+  }
+
+  // Grouped: per-expert m-tile prefix built in LDS from the device offsets.
+  __device__ __forceinline__ static void run_grouped(const Args& a, char* smem, int* pref) {
+    // pref[0..E] = prefix of ceil(rows_e / BM); E <= 1023 (host checked)
+    if (threadIdx.x == 0) {
+      int acc = 0;
+      pref[0] = 0;
+      for (int e = 0; e < a.E; ++e) {
+        const int rows = a.offsets[e + 1] - a.offsets[e];
+        acc += rows > 0 ? (rows + Core::BM - 1) / Core::BM : 0;
+        pref[e + 1] = acc;
+      }
+    }
+    __syncthreads();
+    const int total = pref[a.E] * a.tiles_n;
+    for (int b = blockIdx.x; b < total; b += gridDim.x) {
+      const int mt = b / a.tiles_n, tn = b - mt * a.tiles_n;
+      int lo = 0, hi = a.E - 1;  // largest e with pref[e] <= mt
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pref[mid] <= mt)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      Unit u;
+      u.expert = lo;
+      u.tile = b;
+      u.m0 = a.offsets[lo] + (mt - pref[lo]) * Core::BM;
+      u.m_end = a.offsets[lo + 1];
+      u.n0 = tn * Core::BN;
+      u.kb = 0;
+      u.ke = a.iters;
+      Acc acc;
+      Core::mainloop(a, u, smem, acc);
+      Core::store(a, u, acc);
+    }
+  }
+};
+
+template <class Core, int MODE>
+__global__ __launch_bounds__(Core::NT) void sched_kernel(const Args a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Core::SMEM_BYTES];
+  __shared__ int misc[MODE == MODE_GROUPED ? 1025 : 1];
+  if constexpr (MODE == MODE_DP) Sched<Core>::run_dp(a, smem);
+  if constexpr (MODE == MODE_SPLITK) Sched<Core>::run_splitk(a, smem, misc);
+  if constexpr (MODE == MODE_STREAMK) Sched<Core>::run_streamk(a, smem, misc);
+  if constexpr (MODE == MODE_GROUPED) Sched<Core>::run_grouped(a, smem, misc);
+}
+
+// Host-side launcher: one kernel instantiation per schedule.
+template <class Core>
+hipError_t launch_sched(const Args& a, int grid, hipStream_t s) {
+  switch (a.mode) {
+    case MODE_DP: hipLaunchKernelGGL((sched_kernel<Core, MODE_DP>), dim3(grid), dim3(Core::NT), 0, s, a); break;
+    case MODE_SPLITK: hipLaunchKernelGGL((sched_kernel<Core, MODE_SPLITK>), dim3(grid), dim3(Core::NT), 0, s, a); break;
+    case MODE_STREAMK: hipLaunchKernelGGL((sched_kernel<Core, MODE_STREAMK>), dim3(grid), dim3(Core::NT), 0, s, a); break;
+    case MODE_GROUPED: hipLaunchKernelGGL((sched_kernel<Core, MODE_GROUPED>), dim3(grid), dim3(Core::NT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,257 @@
+// Skinny-M (decode-shaped) GEMM core for gfx950: M <= 16 * MT.
+//
+// The DeepGEMM write-up (section 5.1) notes that the M=1 shape is load-bound
+// and needs its own kernel. Here every wave streams its own k-blocks of B
+// (BN rows) and A (BM rows) -- 256 contiguous bytes per row per block -- from
+// HBM into a private DEPTH-deep LDS ring with buffer_load ... lds, so a wave
+// only ever waits for its own loads (vmcnt) and never for the other waves.
+// The waves of a workgroup cover the same BN columns and take interleaved
+// k-blocks; their accumulators are summed through LDS in wave order at the
+// end, so the result is deterministic. Rows are stored with chunk' = chunk ^
+// (row & 15) over their 16 chunks of 16 bytes, so the 16 rows an MFMA operand
+// read touches hit 16 different bank groups. Work division (DP / split-K /
+// stream-K) is the shared one in qg_sched.hpp.
+//
+// MFMA 16x16 (bf16/fp16 16x16x32, int8 16x16x64): lane l supplies row l % 16
+// and the 16-byte k-slice l / 16 of each operand; output element r of lane l
+// is row 4*(l/16) + r, column l % 16. B rows are the MFMA's first operand and
+// A rows its second, so a lane ends up holding 4 consecutive columns n of one
+// row m of D (one vector store).
+#pragma once
+#include "qg_tile.hpp"
+
+namespace qg {
+
+// NSPLIT_ = false: the waves share the workgroup's BN columns and interleave
+// k-blocks (summed through LDS at the end); true: each wave owns BN / NW
+// columns over the whole k-range (no cross-wave sum).
+template <El E_, int BN_, int NW_, int MT_, int DEPTH_, int BLKB_ = 256, bool NSPLIT_ = false>
+struct SkinnyCfg {
+  static constexpr El E = E_;
+  static constexpr bool NSPLIT = NSPLIT_;
+  static constexpr int BN = BN_, NW = NW_, MT = MT_, DEPTH = DEPTH_;
+  static constexpr int BNW = NSPLIT ? BN / NW : BN;  // columns per wave
+  static constexpr int NT = NW * 64, BM = 16 * MT, TN = BNW / 16;
+  static constexpr int ESIZE = (E_ == El::BF16 || E_ == El::F16) ? 2 : 1;
+  static constexpr int BLKB = BLKB_;              // bytes of k per row per block (256 or 512)
+  static constexpr int CPR = BLKB / 16;           // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;            // rows filled by one 64-lane load
+  static constexpr int STEPS = BLKB / 64;         // MFMA k-steps per block
+  static constexpr int BK = BLKB / ESIZE;         // k elements per block
+  static constexpr int SLOT = (BNW + BM) * BLKB;  // LDS bytes of one wave's ring slot
+  static constexpr int LPS = (BNW + BM) / RPI;    // 64-lane loads per slot
+  static_assert(BLKB == 256 || BLKB == 512, "block bytes");
+  static_assert(NW * DEPTH * SLOT <= 160 * 1024 - 4096, "LDS budget");
+  static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
+  static constexpr bool INT = (E_ == El::I8);
+  static_assert(BNW % 16 == 0 && BNW * (NSPLIT ? NW : 1) == BN && DEPTH >= 1, "skinny tile");
+};
+
+__device__ __forceinline__ f32x4 mfma16_bf16(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f16(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma16_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+template <class Cfg>
+struct Skinny {
+  using S4 = typename AccOf<Cfg::INT>::S4;
+  static constexpr int TN = Cfg::TN, MT = Cfg::MT, NW = Cfg::NW, DEPTH = Cfg::DEPTH;
+  static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BNW = Cfg::BNW;
+  static constexpr int SMEM_BYTES = NW * DEPTH * Cfg::SLOT;  // per-wave rings (reused for the reduction)
+  static_assert(NW * TN * MT * 64 * 16 <= SMEM_BYTES, "reduction space");
+  struct Acc {
+    S4 v[TN][MT];
+  };
+
+  __device__ __forceinline__ static S4 mma(i32x4 b, i32x4 a, S4 c) {
+    if constexpr (Cfg::E == El::BF16) return mfma16_bf16(b, a, c);
+    else if constexpr (Cfg::E == El::F16) return mfma16_f16(b, a, c);
+    else return mfma16_i8(b, a, c);
+  }
+
+  __device__ __forceinline__ static void mainloop(const Args& a, const Unit& u, char* smem, Acc& acc) {
+    const int w = wave_id(), l = lane_id();
+    constexpr int ES = Cfg::ESIZE;
+    const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
+    const uint32_t kbytes = (uint32_t)a.K * ES;
+    const int a_rows = max(0, min(BM, u.m_end - u.m0));
+    const int b_rows = max(0, min(BN, a.N - u.n0));
+    const i32x4 rA = make_rsrc_words((const char*)a.A + (int64_t)u.m0 * lda_b, (uint32_t)(a_rows * lda_b));
+    // N-split: this wave's rows of B start BNW * w rows into the tile
+    const int nw0 = Cfg::NSPLIT ? w * BNW : 0;
+    const int b_rows_w = max(0, min(BNW, b_rows - nw0));
+    const i32x4 rB = make_rsrc_words(
+        (const char*)a.B + (int64_t)u.expert * a.b_batch * ES + (int64_t)(u.n0 + nw0) * ldb_b,
+        (uint32_t)((Cfg::NSPLIT ? b_rows_w : b_rows) * ldb_b));
+    // One 64-lane load fills RPI rows x BLKB bytes of a slot: lane l -> row
+    // l / CPR, physical chunk l % CPR, which holds logical chunk
+    // (l % CPR) ^ (row & 15).
+    constexpr int CPR = Cfg::CPR, RPI = Cfg::RPI;
+    char* ring = smem + w * DEPTH * Cfg::SLOT;
+    const int lrow = l / CPR;
+    constexpr int LB = BNW / RPI, LA = BM / RPI;
+    uint32_t offB[LB], offA[LA], chB[LB], chA[LA];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = i * RPI + lrow;
+      chB[i] = (uint32_t)(((l % CPR) ^ (row & 15)) * 16);
+      offB[i] = (uint32_t)(row * ldb_b) + chB[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int row = i * RPI + lrow;
+      chA[i] = (uint32_t)(((l % CPR) ^ (row & 15)) * 16);
+      offA[i] = (uint32_t)(row * lda_b) + chA[i];
+    }
+    // Loads k-block blk into ring slot d; blocks past the unit read nothing.
+    auto issue = [&](int d, int blk) {
+      char* base = ring + d * Cfg::SLOT;
+      const bool live = blk < u.ke;
+      const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        load_lds_x4(rB, base + i * 1024, live && kk + chB[i] < kbytes ? offB[i] + kk : kOOB);
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        load_lds_x4(rA, base + BNW * Cfg::BLKB + i * 1024, live && kk + chA[i] < kbytes ? offA[i] + kk : kOOB);
+    };
+    // Operand fragments of the block in slot d: step j covers bytes
+    // [64j, 64j+64) of each row; lane l reads row l%16 of each 16-row group at
+    // logical chunk 4j + l/16.
+    constexpr int ST = Cfg::STEPS;
+    i32x4 fb[ST][TN], fa[ST][MT];
+    auto read = [&](int d) {
+      const char* base = ring + d * Cfg::SLOT;
+#pragma unroll
+      for (int j = 0; j < ST; ++j) {
+        const int c = 4 * j + (l >> 4);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int row = tn * 16 + (l & 15);
+          fb[j][tn] = *(const i32x4*)(base + row * Cfg::BLKB + ((c ^ (row & 15)) << 4));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int row = mt * 16 + (l & 15);
+          fa[j][mt] = *(const i32x4*)(base + BNW * Cfg::BLKB + row * Cfg::BLKB + ((c ^ (row & 15)) << 4));
+        }
+      }
+    };
+    auto compute = [&]() {
+#pragma unroll
+      for (int j = 0; j < ST; ++j)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = mma(fb[j][tn], fa[j][mt], acc.v[tn][mt]);
+    };
+
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = S4{};
+
+    const int nk = u.ke - u.kb;
+    // This wave's blocks are kb + w, kb + w + NW, ...; the count is rounded up
+    // to a multiple of DEPTH (the extra blocks read nothing and add zeros) so
+    // exactly DEPTH - 1 blocks are in flight behind the one being consumed.
+    // k-interleaved: block i of this wave is kb + w + i * NW; N-split: kb + i.
+    constexpr int KSTRIDE = Cfg::NSPLIT ? 1 : NW;
+    const int kfirst = Cfg::NSPLIT ? 0 : w;
+    const int count = nk > kfirst ? (nk - kfirst + KSTRIDE - 1) / KSTRIDE : 0;
+    const int rounds = (count + DEPTH - 1) / DEPTH;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, u.kb + kfirst + d * KSTRIDE);
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        wait_vmcnt<Cfg::LPS * (DEPTH - 1)>();
+        asm volatile("" ::: "memory");
+        read(d);
+        // refill the slot as soon as its fragments are in registers
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        asm volatile("" ::: "memory");
+        issue(d, u.kb + kfirst + ((r + 1) * DEPTH + d) * KSTRIDE);
+        compute();
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with its ring before it is reused below
+    if constexpr (Cfg::NSPLIT) return;  // each wave already holds its own columns
+
+    // Sum the waves' partial sums in wave order into wave 0.
+    S4* red = (S4*)smem;
+    if (w > 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[((w * TN + tn) * MT + mt) * 64 + l] = acc.v[tn][mt];
+    }
+    __syncthreads();
+    if (w == 0) {
+      for (int w2 = 1; w2 < NW; ++w2)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] += red[((w2 * TN + tn) * MT + mt) * 64 + l];
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: wave 0 holds the tile (k-interleaved) or each wave its columns (N-split).
+  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc) {
+    if (!Cfg::NSPLIT && wave_id() != 0) return;
+    const int l = lane_id();
+    const int nw0 = Cfg::NSPLIT ? wave_id() * BNW : 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = u.m0 + mt * 16 + (l & 15);
+      if (m >= u.m_end) continue;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int n = u.n0 + nw0 + tn * 16 + 4 * (l >> 4);
+        if (n < a.N) epi_store4(a, m, n, acc.v[tn][mt]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t slot_rsrc(const Args& a, int slot) {
+    return make_rsrc((const char*)a.partials + (size_t)slot * (BM * BN * 4), BM * BN * 4);
+  }
+  // Partial tile layout: [wave (N-split) ][tn][mt][lane] x 16 bytes.
+  __device__ __forceinline__ static uint32_t pofs(int tn, int mt) {
+    const int w = Cfg::NSPLIT ? wave_id() : 0;
+    return (uint32_t)((((w * TN + tn) * MT + mt) * 64 + lane_id()) * 16);
+  }
+  __device__ __forceinline__ static void write_partial(const Args& a, int slot, Acc& acc) {
+    if (!Cfg::NSPLIT && wave_id() != 0) return;
+    const auto r = slot_rsrc(a, slot);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) store_sc1_x4(r, pofs(tn, mt), __builtin_bit_cast(i32x4, acc.v[tn][mt]));
+  }
+  __device__ __forceinline__ static void add_partial(const Args& a, int slot, Acc& tot, bool first) {
+    if (!Cfg::NSPLIT && wave_id() != 0) return;
+    const auto r = slot_rsrc(a, slot);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const S4 x = __builtin_bit_cast(S4, load_sc1_x4(r, pofs(tn, mt)));
+        tot.v[tn][mt] = first ? x : tot.v[tn][mt] + x;
+      }
+  }
+};
+
+template <class Cfg>
+hipError_t launch_skinny(const Args& a, int grid, hipStream_t s) {
+  return launch_sched<Skinny<Cfg>>(a, grid, s);
+}
+
+}  // namespace qg

@@ -129,9 +129,8 @@ def test_plan_streamk_matches_planner(g):
     op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=256)
     d = dict(kv.split("=") for kv in g.plan(op, Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
     assert d["schedule"] == "streamk" and d["programs"] == "256" and d["grid"] == "256"
-    name = d["kernel"]
-    bm, bn = map(int, re.search(r"_(\d+)x(\d+)_", name).groups())
-    pl = streamk_plan(M, N, K, bm, bn, 64, 256)
+    bm, bn, bk = int(d["bm"]), int(d["bn"]), int(d["bk"])
+    pl = streamk_plan(M, N, K, bm, bn, bk, 256)
     assert int(d["tiles"]) == pl["total_tiles"]
     assert int(d["partials"]) == 2 * 256 * bm * bn * 4
 
@@ -155,8 +154,8 @@ def test_tuning_sequence(g):
 
 
 CACHE = """qgemm-cache 1 arch=gfx950 entries=2
-16|bf16.bf16.-.bf16.q00.e0.n4096.k14336 kernel=tile_BF16_32x64_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
-4096|bf16.bf16.-.bf16.q00.e0.n4096.k4096 kernel=tile_BF16_128x128_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
+16|bf16.bf16.-.bf16.q00.e0.n4096.k14336 kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
+4096|bf16.bf16.-.bf16.q00.e0.n4096.k4096 kernel=tile_BF16_128x128x128b_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
 """
 
 
@@ -172,9 +171,9 @@ def test_cache_import_export_roundtrip_and_lookup():
     assert g2.import_(out) == qg.OK and g2.export() == out
     # the DEFAULT policy uses the cached choice, also for an M that maps to the same bucket
     Ad, Bd, Dd = dense(16, 4096, 14336)
-    assert "kernel=tile_BF16_32x64_w1x2_s6 schedule=splitk split=4" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    assert "kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
     Ad, Bd, Dd = dense(11, 4096, 14336)
-    assert "kernel=tile_BF16_32x64_w1x2_s6" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    assert "kernel=tile_BF16_32x64x128b_w1x2_s6" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
     # REUSE misses where nothing is cached
     Ad, Bd, Dd = dense(16, 2048, 2048)
     with pytest.raises(qg.QGemmError) as e:
@@ -188,7 +187,7 @@ def test_cache_import_export_roundtrip_and_lookup():
     "qgemm-cache 2 arch=gfx950 entries=0\n",
     "qgemm-cache 1 arch=gfx942 entries=0\n",
     CACHE.replace("entries=2", "entries=3"),
-    CACHE.replace("kernel=tile_BF16_32x64_w1x2_s6", "kernel=no_such_kernel"),
+    CACHE.replace("kernel=tile_BF16_32x64x128b_w1x2_s6", "kernel=no_such_kernel"),
     CACHE.replace("schedule=dp", "schedule=zigzag"),
     CACHE.replace("split=4", "split=x"),
     CACHE.replace("us=90.000", "us=90.000 extra"),

@@ -35,8 +35,8 @@ def test_tiny_config(g, ws):
     check_against_oracle(p, D, what="256^3 bf16 alpha 1.5 beta 0.5 fp32 out")
 
 
-@pytest.mark.parametrize("kname", ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4",
-                                   "tile_BF16_32x128_w1x4_s4", "tile_BF16_32x64_w1x2_s6"])
+@pytest.mark.parametrize("kname", ["tile_BF16_256x256x128b_w2x4_s2", "tile_BF16_128x128x128b_w2x2_s4",
+                                   "tile_BF16_32x128x128b_w1x4_s4", "tile_BF16_32x64x128b_w1x2_s6"])
 @pytest.mark.parametrize("shape", [(300, 200, 136), (257, 513, 264), (64, 64, 64), (33, 1000, 72), (1, 130, 8)])
 def test_ragged_each_kernel(g, ws, kname, shape):
     M, N, K = shape
@@ -58,14 +58,14 @@ def test_output_and_c_types(g, ws, out, cdt):
 def test_odd_and_even_k_tile_counts(g, ws, nk):
     # 64 bf16 per k-tile: an odd k-tile count changes which ring stage the last tile uses
     p = synth.dense_problem(256, 256, 64 * nk, "bf16", "f32", dist="normal", seed=nk)
-    for kname in ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4", "tile_BF16_32x64_w1x2_s6"]:
+    for kname in ["tile_BF16_256x256x128b_w2x4_s2", "tile_BF16_128x128x128b_w2x2_s4", "tile_BF16_32x64x128b_w1x2_s6"]:
         op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
         check_against_oracle(p, Run(g, p, ws).run(op), what=f"{kname} k-tiles {nk}")
 
 
 def test_fp16_ragged(g, ws):
     p = synth.dense_problem(200, 328, 456, "f16", "f16", c_dtype="f16", alpha=1.0, beta=1.0, dist="uniform", seed=9)
-    for kname in ["tile_F16_256x256_w2x4_s2", "tile_F16_128x128_w2x2_s4", "tile_F16_32x128_w1x4_s4"]:
+    for kname in ["tile_F16_256x256x128b_w2x4_s2", "tile_F16_128x128x128b_w2x2_s4", "tile_F16_32x128x128b_w1x4_s4"]:
         op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
         check_against_oracle(p, Run(g, p, ws).run(op), what=kname)
 
@@ -74,7 +74,7 @@ def test_fp16_ragged(g, ws):
 def test_splitk_matches_oracle_and_leaves_barriers_zero(g, ws, split):
     p = synth.dense_problem(48, 520, 2056, "bf16", "bf16", c_dtype="bf16", alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02, seed=11)
     r = Run(g, p, ws)
-    for kname in ["tile_BF16_32x128_w1x4_s4", "tile_BF16_128x128_w2x2_s4"]:
+    for kname in ["tile_BF16_32x128x128b_w1x4_s4", "tile_BF16_128x128x128b_w2x2_s4"]:
         op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=split, kernel=kidx(kname))
         print(kname, r.plan(op), flush=True)
         D1 = r.run(op)
@@ -88,7 +88,7 @@ def test_splitk_matches_oracle_and_leaves_barriers_zero(g, ws, split):
 def test_streamk(g, ws, programs):
     p = synth.dense_problem(200, 700, 1000, "bf16", "f32", c_dtype="f32", alpha=1.0, beta=0.5, dist="uniform", seed=13)
     r = Run(g, p, ws)
-    for kname in ["tile_BF16_128x128_w2x2_s4", "tile_BF16_32x128_w1x4_s4"]:
+    for kname in ["tile_BF16_128x128x128b_w2x2_s4", "tile_BF16_32x128x128b_w1x4_s4"]:
         op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=programs, kernel=kidx(kname))
         print(kname, r.plan(op), flush=True)
         D1 = r.run(op)
@@ -127,7 +127,7 @@ def test_int8_exact(g, ws, shape):
     M, N, K = shape
     p = synth.dense_problem(M, N, K, "i8", "i32", c_dtype="i32", alpha=1.0, beta=1.0, seed=M * 3 + K)
     r = Run(g, p, ws)
-    for kname in ["tile_I8_256x256_w2x4_s2", "tile_I8_128x128_w2x2_s4", "tile_I8_32x128_w1x4_s4"]:
+    for kname in ["tile_I8_256x256x128b_w2x4_s2", "tile_I8_128x128x128b_w2x2_s4", "tile_I8_32x128x128b_w1x4_s4"]:
         op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
         check_against_oracle(p, r.run(op), what=f"{kname} {shape}")
 
@@ -152,7 +152,7 @@ def test_grouped_small_with_empty_experts(g, ws):
     counts = np.array([5, 0, 300, 1, 0, 129, 256, 0], dtype=np.int32)
     p = synth.grouped_problem(counts, 384, 256, seed=17)
     r = Run(g, p, ws)
-    for kname in ["tile_BF16_256x256_w2x4_s2", "tile_BF16_128x128_w2x2_s4"]:
+    for kname in ["tile_BF16_256x256x128b_w2x4_s2", "tile_BF16_128x128x128b_w2x2_s4"]:
         op = qg.operation(policy=qg.POLICY_FORCE, kernel=kidx(kname))
         print(kname, r.plan(op), flush=True)
         check_against_oracle(p, r.run(op), what=f"grouped {kname}")
@@ -162,3 +162,50 @@ def test_tiny_config_plan_is_logged(g, ws):
     p = synth.config_tiny()
     desc = Run(g, p, ws).plan()
     assert desc.startswith("kernel=tile_BF16_")
+
+
+# ---------------------------------------------------------------- skinny-M streaming kernels
+SKINNY = ["skinny_BF16_1x16x16x256b_w4_d4_n0", "skinny_BF16_1x16x128x256b_w8_d2_n1", "skinny_BF16_1x16x64x256b_w2_d2_n0",
+          "skinny_BF16_2x16x32x256b_w4_d2_n0", "skinny_BF16_1x16x64x256b_w4_d3_n1"]
+
+
+@pytest.mark.parametrize("kname", SKINNY)
+@pytest.mark.parametrize("shape", [(1, 130, 520), (16, 4096, 1032), (5, 77, 8), (13, 200, 4104)])
+@pytest.mark.parametrize("sched", ["dp", "split3", "streamk"])
+def test_skinny_kernels(g, ws, kname, shape, sched):
+    M, N, K = shape
+    if kname.startswith("skinny_BF16_2x"):
+        M = M + 16  # exercise the second 16-row tile
+    p = synth.dense_problem(M, N, K, "bf16", "bf16", c_dtype="bf16", alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02, seed=N + K)
+    r = Run(g, p, ws)
+    if sched == "dp":
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+    elif sched == "split3":
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=3, kernel=kidx(kname))
+    else:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=37, kernel=kidx(kname))
+    print(kname, shape, r.plan(op), flush=True)
+    D1 = r.run(op)
+    check_against_oracle(p, D1, what=f"{kname} {shape} {sched}")
+    assert int(ws.barriers.abs().sum().item()) == 0
+    assert np.array_equal(D1, r.run(op))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_skinny_decode_full_size_split8(g, ws, M):
+    p = synth.config_decode(M=M)
+    r = Run(g, p, ws)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8, kernel=kidx("skinny_BF16_1x16x32x256b_w4_d3_n0"))
+    print(r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"skinny decode M={M}")
+
+
+def test_skinny_fp16_and_int8(g, ws):
+    p = synth.dense_problem(9, 300, 2056, "f16", "f16", c_dtype="f32", alpha=0.5, beta=2.0, dist="uniform", seed=3)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=4, kernel=kidx("skinny_F16_1x16x32x256b_w4_d3_n0"))
+    check_against_oracle(p, Run(g, p, ws).run(op), what="skinny f16")
+    p = synth.dense_problem(16, 4096, 14336, "i8", "i32", c_dtype="i32", alpha=1.0, beta=1.0, seed=8)
+    for sched in (qg.SCHED_SPLITK, qg.SCHED_STREAMK):
+        for kn in ("skinny_I8_1x16x32x256b_w4_d3_n0", "skinny_I8_1x16x128x256b_w8_d2_n1"):
+            op = qg.operation(policy=qg.POLICY_FORCE, schedule=sched, split_k=8, programs=256, kernel=kidx(kn))
+            check_against_oracle(p, Run(g, p, ws).run(op), what=f"skinny int8 decode {kn}")
