@@ -172,7 +172,19 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     if (alpha != 1.f || !(beta == 0.f || beta == 1.f)) return QG_ERR_UNSUPPORTED;
   } else if (float16ish) {
     if (p.tb == QG_U4) {
-      return QG_ERR_UNSUPPORTED;  // int4 weight-only kernels are registered separately
+      // weight-only int4: bf16 A, 128-deep groups of fp16 scales in V
+      if (p.ta != QG_BF16 || p.qa != QG_QUANT_NONE || p.qb != QG_QUANT_INT4_ZP) return QG_ERR_UNSUPPORTED;
+      if (op->quant_b.group_k != 128 || p.K % 128) return QG_ERR_UNSUPPORTED;
+      if (op->quant_b.zero_point < 0 || op->quant_b.zero_point > 15) return QG_ERR_INVALID_ARG;
+      if (grouped) return QG_ERR_UNSUPPORTED;
+      if (!Vd || (p.M > 0 && p.N > 0 && p.K > 0 && !V)) return QG_ERR_INVALID_ARG;
+      if ((st = check_layout(Vd))) return st;
+      if (Vd->type != QG_F16 || Vd->rows != p.N || Vd->cols != p.K / 128 || Vd->ld < Vd->cols) return QG_ERR_INVALID_ARG;
+      if ((Vd->ld * 2) % 16 || !aligned16(V)) return QG_ERR_ALIGNMENT;
+      p.V = V;
+      p.ldv = Vd->ld;
+      p.zp = op->quant_b.zero_point;
+      p.group_k = 128;
     } else if (p.tb != p.ta || p.qa || p.qb) {
       return QG_ERR_UNSUPPORTED;
     }
@@ -193,7 +205,9 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   p.lda = Ad->ld;
   p.ldb = Bd->ld;
   p.ldd = Dd->ld;
-  if (p.lda < p.K || p.ldb < p.K || p.ldd < p.N) return QG_ERR_INVALID_ARG;
+  const int64_t b_row_elems = p.tb == QG_U4 ? p.ldb * 8 : p.ldb;  // U4: ld counts words
+  if (p.lda < p.K || b_row_elems < p.K || p.ldd < p.N) return QG_ERR_INVALID_ARG;
+  if (p.tb == QG_U4 && p.K % 8) return QG_ERR_ALIGNMENT;
   if ((p.lda * esize(p.ta)) % 16 || (p.ldb * esize(p.tb)) % 16 || (p.ldd * esize(p.td)) % 16) return QG_ERR_ALIGNMENT;
   if ((p.K * esize(p.ta)) % 16) return QG_ERR_ALIGNMENT;
   if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return QG_ERR_ALIGNMENT;
@@ -229,6 +243,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
 
 // ---- registry filtering ("Context") ------------------------------------------
 bool compatible(const KernelInfo& k, const Problem& p) {
+  if (k.family == FAM_W4) return p.ta == QG_BF16 && p.tb == QG_U4 && p.E == 0;
   if (k.family != FAM_TILE && k.family != FAM_SKINNY) return false;
   if (k.family == FAM_SKINNY && p.M > k.bm && p.E == 0) return false;  // skinny tiles cover all rows
   return k.in_type == p.ta && p.tb == p.ta;
@@ -390,6 +405,21 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, i
     return c;
   }
   const bool ws_ok = ws && ws->partials && ws->barriers;
+  if (p.tb == QG_U4) {
+    c.kernel = kernel_by_shape(p, p.M <= 32 ? 32 : 64, 256);
+    if (c.kernel < 0) return c;
+    const KernelInfo& k = kKernels[c.kernel];
+    const int64_t tiles = cdiv(p.M, k.bm) * cdiv(p.N, k.bn), iters = cdiv(p.K, k.bk);
+    c.mode = MODE_DP;
+    if (forced_mode < 0 && tiles < cus && iters >= 4 && ws_ok) {
+      const int s = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(cus, tiles), iters / 2));
+      if (s > 1 && (size_t)tiles * s * k.slot_bytes <= ws->partials_size && (size_t)tiles * 4 <= ws->barriers_size) {
+        c.mode = MODE_SPLITK;
+        c.split = s;
+      }
+    }
+    return c;
+  }
   if (p.M <= 32) {
     // Skinny GEMM: aim for about one workgroup per compute unit.
     int64_t target = cdiv(p.N, cus);

@@ -1,5 +1,5 @@
 // Explicit instantiations of the bf16 kernels listed in qg_kernel_list.inc.
-#include "qg_skinny.hpp"
+#include "qg_w4.hpp"
 
 namespace qg {
 #define QG_TILE_BF16(BM, BN, WM, WN, ST, RB)
@@ -14,5 +14,6 @@ namespace qg {
   template hipError_t launch_tile<TileCfg<El::BF16, BM, BN, WM, WN, ST, RB>>(const Args&, int, hipStream_t);
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) \
   template hipError_t launch_skinny<SkinnyCfg<El::BF16, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
+#define QG_W4(BM, BN, NW, ST) template hipError_t launch_w4<W4Cfg<BM, BN, NW, ST>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"
 }  // namespace qg

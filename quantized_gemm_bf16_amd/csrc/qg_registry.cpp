@@ -1,7 +1,7 @@
 // The kernel registry table ("all registered GEMM kernels for the current
 // device", page "InternLM Lmdeploy Gemm Interface", Description).
 #include "qg_registry.hpp"
-#include "qg_skinny.hpp"
+#include "qg_w4.hpp"
 
 namespace qg {
 
@@ -15,7 +15,10 @@ namespace qg {
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) QG_DECL_SK(BF16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS) QG_DECL_SK(F16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) QG_DECL_SK(I8, BN, NW, MT, DP, BB, NS)
+#define QG_W4(BM, BN, NW, ST) \
+  extern template hipError_t launch_w4<W4Cfg<BM, BN, NW, ST>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"
+#undef QG_W4
 #undef QG_TILE_BF16
 #undef QG_TILE_F16
 #undef QG_TILE_I8
@@ -37,6 +40,10 @@ namespace qg {
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(BF16, DT_BF16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(F16, DT_F16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(I8, DT_I8, BN, NW, MT, DP, BB, NS)
+
+#define QG_W4(BM, BN, NW, ST)                                                                          \
+  {"w4_BF16_" #BM "x" #BN "_w" #NW "_s" #ST, FAM_W4, DT_BF16, BM, BN, 128, ST, NW * 64, BM * BN * 4, \
+   &launch_w4<W4Cfg<BM, BN, NW, ST>>},
 
 // (not const: a const table would also be placed in device constant memory)
 KernelInfo kKernels[] = {

@@ -35,6 +35,10 @@ def decode_c(p):
     return c.astype(np.float64)
 
 
+def kind_of(p):
+    return p["kind"]
+
+
 class Run:
     """Uploads a problem once; `run(op)` launches and returns D on the host."""
 
@@ -53,7 +57,15 @@ class Run:
             cp[:, :N] = p["C"]
             self.C = dev(cp)
         self.U = dev(p["U"]) if p.get("U") is not None else None
-        self.V = dev(p["V"]) if p.get("V") is not None else None
+        self.V = None
+        if p.get("V") is not None:
+            V = p["V"]
+            if kind_of(p) == "w4a16":  # scale rows padded to a 16-byte pitch
+                self.ldv = -(-V.shape[1] // 8) * 8
+                Vp = np.zeros((V.shape[0], self.ldv), dtype=V.dtype)
+                Vp[:, :V.shape[1]] = V
+                V = Vp
+            self.V = dev(V)
         self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") if self.out != "i32" \
             else torch.full((M, self.ldn), -7, dtype=torch.int32, device="cuda")
         kind = p["kind"]
@@ -71,7 +83,7 @@ class Run:
         self.Cd = qg.layout(p["c_dtype"], M, N, ld=self.ldn) if self.C is not None else None
         self.Ud = self.Vd = None
         if kind == "w4a16":
-            self.Vd = qg.layout("f16", N, p["V"].shape[1])
+            self.Vd = qg.layout("f16", N, p["V"].shape[1], ld=self.ldv)
         if p.get("U") is not None and kind == "grouped":
             self.Ud = qg.layout("f32", M, p["U"].shape[1], num=p["E"], offsets=self.off.data_ptr())
             self.Vd = qg.layout("f32", p["V"].shape[1], p["V"].shape[2], num=p["E"], stride=p["V"].shape[1] * p["V"].shape[2])

@@ -209,3 +209,26 @@ def test_export_buffer_too_small():
     buf = ctypes.create_string_buffer(4)
     assert qg.lib.qg_export(g.h, buf, 4, ctypes.byref(n)) == qg.ERR_BUFFER_SMALL
     assert n.value == len(g.export()) + 1
+
+
+def test_w4a16_validation(g):
+    M, N, K = 64, 512, 1024
+    Ad = qg.layout("bf16", M, K)
+    Bd = qg.layout("u4", N, K)  # ld = K/8 words
+    Dd = qg.layout("bf16", M, N)
+    Vd = qg.layout("f16", N, K // 128)
+    q = qg.operation(quant_b=(qg.QUANT_INT4_ZP, 128, 1, 8))
+    # missing scales
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    # wrong group size / K not a multiple of the group
+    q64 = qg.operation(quant_b=(qg.QUANT_INT4_ZP, 64, 1, 8))
+    assert run(g, op=q64, Ad=Ad, Bd=Bd, Dd=Dd, V=FAKE, Vd=qg.layout("f16", N, K // 64)) == qg.ERR_UNSUPPORTED
+    # scale shape mismatch, misaligned scale rows
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd, V=FAKE, Vd=qg.layout("f16", N, K // 128 + 1)) == qg.ERR_INVALID_ARG
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd, V=FAKE, Vd=qg.layout("f16", N, 8, ld=12)) == qg.ERR_ALIGNMENT
+    # u4 without the quant descriptor, fp16 A
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, V=FAKE, Vd=Vd) == qg.ERR_UNSUPPORTED
+    assert run(g, op=q, Ad=qg.layout("f16", M, K), Bd=Bd, Dd=Dd, V=FAKE, Vd=Vd) == qg.ERR_UNSUPPORTED
+    # a valid request plans onto the int4 kernel with split-K
+    d = dict(kv.split("=") for kv in g.plan(q, Ad, None, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["kernel"].startswith("w4_BF16_") and d["bk"] == "128"
