@@ -155,6 +155,11 @@ def gemm(p: dict, rows=None, splits: int = 1, alpha=None, beta=None):
         B = c(p["B"])
         st.tb = _DT[p["in_dtype"]]
         st.B, st.ldb = _ptr(B), K
+        if p["in_dtype"] == "e4m3":
+            U, V = c(p["U"]), c(p["V"])
+            st.qa = st.qb = Q_BLOCK
+            st.U, st.ldu, st.gm_a, st.gk_a = _ptr(U), U.shape[1], 1, p["group_k"]
+            st.V, st.ldv, st.gn_b, st.gk_b = _ptr(V), V.shape[1], p["group_n"], p["group_k"]
     if rows is None:
         n = M
         rp = None

@@ -57,9 +57,16 @@ __device__ __forceinline__ void load_lds_x4(const i32x4& rsrc, void* lds_wave_ba
       : "s"(m0v), "v"(voff), "s"(rsrc)
       : "memory", "m0");
 }
-// One dword per lane, written to LDS at lds_wave_base + 4 * lane.
-__device__ __forceinline__ void load_lds_x1(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, voff, 0, 0, 0);
+// One dword per lane, written to LDS at lds_wave_base + 4 * lane (inline
+// assembly for the same reason as load_lds_x4).
+__device__ __forceinline__ void load_lds_x1a(const i32x4& rsrc, void* lds_wave_base, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
 }
 
 // 16-byte buffer store / load with the sc1 cache-policy bit (coherent at agent

@@ -190,7 +190,30 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     }
     if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16)) return QG_ERR_UNSUPPORTED;
   } else if (p.ta == QG_E4M3) {
-    return QG_ERR_UNSUPPORTED;  // fp8 block-scaled kernels are registered separately
+    // block-scaled fp8: U fp32 per row and 128-deep k group, V fp32 per
+    // 128 x 128 block of B (per expert when grouped)
+    if (p.tb != QG_E4M3 || p.qa != QG_QUANT_BLOCK_F32 || p.qb != QG_QUANT_BLOCK_F32) return QG_ERR_UNSUPPORTED;
+    if (op->quant_a.group_k != 128 || op->quant_b.group_k != 128 || op->quant_a.group_mn != 1 ||
+        op->quant_b.group_mn != 128)
+      return QG_ERR_UNSUPPORTED;
+    if (!Ud || !Vd) return QG_ERR_INVALID_ARG;
+    if ((st = check_layout(Ud)) || (st = check_layout(Vd))) return st;
+    if (Ud->type != QG_F32 || Vd->type != QG_F32) return QG_ERR_UNSUPPORTED;
+    const int64_t kg = cdiv(p.K, 128);
+    if (Ud->rows != p.M || Ud->cols != kg || Ud->ld < kg) return QG_ERR_INVALID_ARG;
+    if (Vd->rows != cdiv(p.N, 128) || Vd->cols != kg || Vd->ld < kg) return QG_ERR_INVALID_ARG;
+    if (p.M > 0 && p.N > 0 && p.K > 0 && (!U || !V)) return QG_ERR_INVALID_ARG;
+    if ((Ud->ld * 4) % 16 || (Vd->ld * 4) % 16 || !aligned16(U) || !aligned16(V)) return QG_ERR_ALIGNMENT;
+    if (grouped) {
+      if (Vd->num != Ad->num) return QG_ERR_INVALID_ARG;
+      p.v_batch = Vd->stride;
+      if (p.v_batch < Vd->rows * Vd->ld) return QG_ERR_INVALID_ARG;
+    }
+    p.U = U;
+    p.V = V;
+    p.ldu = Ud->ld;
+    p.ldv = Vd->ld;
+    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16)) return QG_ERR_UNSUPPORTED;
   } else {
     return QG_ERR_UNSUPPORTED;
   }
@@ -244,6 +267,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
 // ---- registry filtering ("Context") ------------------------------------------
 bool compatible(const KernelInfo& k, const Problem& p) {
   if (k.family == FAM_W4) return p.ta == QG_BF16 && p.tb == QG_U4 && p.E == 0;
+  if (k.family == FAM_F8) return p.ta == QG_E4M3 && p.tb == QG_E4M3;
   if (k.family != FAM_TILE && k.family != FAM_SKINNY) return false;
   if (k.family == FAM_SKINNY && p.M > k.bm && p.E == 0) return false;  // skinny tiles cover all rows
   return k.in_type == p.ta && p.tb == p.ta;
@@ -397,6 +421,11 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, i
                  int forced_split = 0) {
   Choice c;
   const int cus = h->cus;
+  if (p.E > 0 && p.ta == QG_E4M3) {
+    c.kernel = kernel_by_shape(p, 128, 256);
+    c.mode = MODE_GROUPED;
+    return c;
+  }
   if (p.E > 0) {
     const int64_t avg = p.M / std::max(1, p.E);
     c.kernel = kernel_by_shape(p, avg >= 256 ? 256 : 128, avg >= 256 ? 256 : 128);
@@ -420,7 +449,9 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, i
     }
     return c;
   }
-  if (p.M <= 32) {
+  if (p.ta == QG_E4M3) {
+    c.kernel = kernel_by_shape(p, p.M <= 64 ? 64 : 128, 256);
+  } else if (p.M <= 32) {
     // Skinny GEMM: aim for about one workgroup per compute unit.
     int64_t target = cdiv(p.N, cus);
     if (forced_mode == MODE_SPLITK && forced_split > 1) target = cdiv(p.N * forced_split, cus);

@@ -15,5 +15,6 @@ namespace qg {
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) \
   template hipError_t launch_skinny<SkinnyCfg<El::I8, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
 #define QG_W4(BM, BN, NW, ST)
+#define QG_F8(BM, BN, WM, WN, ST)
 #include "qg_kernel_list.inc"
 }  // namespace qg

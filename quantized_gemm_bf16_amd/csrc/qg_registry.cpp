@@ -2,6 +2,7 @@
 // device", page "InternLM Lmdeploy Gemm Interface", Description).
 #include "qg_registry.hpp"
 #include "qg_w4.hpp"
+#include "qg_fp8.hpp"
 
 namespace qg {
 
@@ -17,8 +18,11 @@ namespace qg {
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) QG_DECL_SK(I8, BN, NW, MT, DP, BB, NS)
 #define QG_W4(BM, BN, NW, ST) \
   extern template hipError_t launch_w4<W4Cfg<BM, BN, NW, ST>>(const Args&, int, hipStream_t);
+#define QG_F8(BM, BN, WM, WN, ST) \
+  extern template hipError_t launch_f8<F8Cfg<BM, BN, WM, WN, ST>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"
 #undef QG_W4
+#undef QG_F8
 #undef QG_TILE_BF16
 #undef QG_TILE_F16
 #undef QG_TILE_I8
@@ -44,6 +48,10 @@ namespace qg {
 #define QG_W4(BM, BN, NW, ST)                                                                          \
   {"w4_BF16_" #BM "x" #BN "_w" #NW "_s" #ST, FAM_W4, DT_BF16, BM, BN, 128, ST, NW * 64, BM * BN * 4, \
    &launch_w4<W4Cfg<BM, BN, NW, ST>>},
+
+#define QG_F8(BM, BN, WM, WN, ST)                                                                         \
+  {"f8_E4M3_" #BM "x" #BN "_w" #WM "x" #WN "_s" #ST, FAM_F8, DT_E4M3, BM, BN, 128, ST, WM * WN * 64, BM * BN * 4, \
+   &launch_f8<F8Cfg<BM, BN, WM, WN, ST>>},
 
 // (not const: a const table would also be placed in device constant memory)
 KernelInfo kKernels[] = {

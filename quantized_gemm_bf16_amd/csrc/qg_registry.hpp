@@ -5,7 +5,7 @@
 
 namespace qg {
 
-enum KernelFamily : int { FAM_TILE = 0, FAM_SKINNY = 1, FAM_W4 = 2 };
+enum KernelFamily : int { FAM_TILE = 0, FAM_SKINNY = 1, FAM_W4 = 2, FAM_F8 = 3 };
 
 typedef hipError_t (*LaunchFn)(const Args& a, int grid, hipStream_t s);
 

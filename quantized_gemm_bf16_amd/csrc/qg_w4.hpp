@@ -46,17 +46,6 @@ struct W4Cfg {
   static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// One dword per lane into LDS at lds_wave_base + 4 * lane.
-__device__ __forceinline__ void load_lds_x1a(const i32x4& rsrc, void* lds_wave_base, uint32_t voff) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave_base);
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds"
-      :
-      : "s"(m0v), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
 template <class Cfg>
 struct W4 {
   static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, TN = Cfg::TN, MT = Cfg::MT;

@@ -180,6 +180,21 @@ def dense_problem(M, N, K, in_dtype=BF16, out_dtype=BF16, c_dtype=None, alpha=1.
     return p
 
 
+def dense_fp8_problem(M, N, K, out_dtype=BF16, c_dtype=None, alpha=1.0, beta=0.0, seed=SEED_A,
+                      a_std=1.0, b_std=0.02, c_std=1.0, gk=128, gn_b=128):
+    """Block-scaled fp8 GEMM: A ~ N(0,a_std) quantised per (row, 128-k) group -> U [M, K/128];
+    B ~ N(0,b_std) per 128x128 block -> V [N/128, K/128]; codes e4m3. C [M,N] ~ N(0,c_std)."""
+    a = normal((M, K), a_std, seed)
+    b = normal((N, K), b_std, seed + (SEED_B - SEED_A))
+    qa, su = quantize_e4m3(a, 1, gk)
+    qb, sv = quantize_e4m3(b, gn_b, gk)
+    p = dict(kind="dense", M=M, N=N, K=K, in_dtype=E4M3, out_dtype=out_dtype, c_dtype=c_dtype,
+             alpha=float(alpha), beta=float(beta), A=qa, B=qb, U=su, V=sv, group_k=gk, group_n=gn_b)
+    if c_dtype is not None:
+        p["C"] = to_storage(normal((M, N), c_std, seed + (SEED_C - SEED_A)), c_dtype)
+    return p
+
+
 def w4a16_problem(M, N, K, group=128, seed=SEED_A, out_dtype=BF16, a_std=1.0,
                   s_lo=0.005, s_hi=0.02, zero_point=8):
     """A bf16 [M,K] ~ N(0,a_std); B int4 nibbles uniform 0..15 packed [N, K/8];

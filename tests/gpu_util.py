@@ -56,16 +56,22 @@ class Run:
             cp = np.zeros((M, self.ldn), dtype=p["C"].dtype)
             cp[:, :N] = p["C"]
             self.C = dev(cp)
-        self.U = dev(p["U"]) if p.get("U") is not None else None
+        # scale rows padded to a 16-byte pitch
+        self.U = None
+        if p.get("U") is not None:
+            U = p["U"]
+            self.ldu = -(-U.shape[1] // 4) * 4
+            Up = np.zeros((U.shape[0], self.ldu), dtype=U.dtype)
+            Up[:, :U.shape[1]] = U
+            self.U = dev(Up)
         self.V = None
         if p.get("V") is not None:
             V = p["V"]
-            if kind_of(p) == "w4a16":  # scale rows padded to a 16-byte pitch
-                self.ldv = -(-V.shape[1] // 8) * 8
-                Vp = np.zeros((V.shape[0], self.ldv), dtype=V.dtype)
-                Vp[:, :V.shape[1]] = V
-                V = Vp
-            self.V = dev(V)
+            per = 8 if V.dtype == np.uint16 else 4
+            self.ldv = -(-V.shape[-1] // per) * per
+            Vp = np.zeros(V.shape[:-1] + (self.ldv,), dtype=V.dtype)
+            Vp[..., :V.shape[-1]] = V
+            self.V = dev(Vp)
         self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") if self.out != "i32" \
             else torch.full((M, self.ldn), -7, dtype=torch.int32, device="cuda")
         kind = p["kind"]
@@ -85,13 +91,17 @@ class Run:
         if kind == "w4a16":
             self.Vd = qg.layout("f16", N, p["V"].shape[1], ld=self.ldv)
         if p.get("U") is not None and kind == "grouped":
-            self.Ud = qg.layout("f32", M, p["U"].shape[1], num=p["E"], offsets=self.off.data_ptr())
-            self.Vd = qg.layout("f32", p["V"].shape[1], p["V"].shape[2], num=p["E"], stride=p["V"].shape[1] * p["V"].shape[2])
+            nb, kg = p["V"].shape[1], p["V"].shape[2]
+            self.Ud = qg.layout("f32", M, p["U"].shape[1], ld=self.ldu, num=p["E"], offsets=self.off.data_ptr())
+            self.Vd = qg.layout("f32", nb, kg, ld=self.ldv, num=p["E"], stride=nb * self.ldv)
+        elif p.get("U") is not None:
+            self.Ud = qg.layout("f32", M, p["U"].shape[1], ld=self.ldu)
+            self.Vd = qg.layout("f32", p["V"].shape[0], p["V"].shape[1], ld=self.ldv)
 
     def op(self, **kw):
         if self.p["kind"] == "w4a16":
             kw.setdefault("quant_b", (qg.QUANT_INT4_ZP, self.p["group"], 1, self.p["zero_point"]))
-        if self.p["kind"] == "grouped" and self.p["in_dtype"] == "e4m3":
+        if self.p["in_dtype"] == "e4m3":
             kw.setdefault("quant_a", (qg.QUANT_BLOCK_F32, self.p["group_k"], 1, 0))
             kw.setdefault("quant_b", (qg.QUANT_BLOCK_F32, self.p["group_k"], self.p["group_n"], 0))
         return qg.operation(**kw)

@@ -232,3 +232,45 @@ def test_w4a16_validation(g):
     # a valid request plans onto the int4 kernel with split-K
     d = dict(kv.split("=") for kv in g.plan(q, Ad, None, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).split())
     assert d["kernel"].startswith("w4_BF16_") and d["bk"] == "128"
+
+
+def test_fp8_block_scaled_validation(g):
+    M, N, K = 96, 384, 640
+    Ad = qg.layout("e4m3", M, K)
+    Bd = qg.layout("e4m3", N, K)
+    Dd = qg.layout("bf16", M, N)
+    Ud = qg.layout("f32", M, K // 128, ld=8)
+    Vd = qg.layout("f32", N // 128, K // 128, ld=8)
+    q = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 128, 1, 0), quant_b=(qg.QUANT_BLOCK_F32, 128, 128, 0))
+    ok = dict(Ad=Ad, Bd=Bd, Dd=Dd, U=FAKE, Ud=Ud, V=FAKE, Vd=Vd)
+    # missing scales, or quant descriptors that are not 1x128 / 128x128 blocks
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, **ok) == qg.ERR_UNSUPPORTED
+    q_bad = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 128, 128, 0), quant_b=(qg.QUANT_BLOCK_F32, 128, 128, 0))
+    assert run(g, op=q_bad, **ok) == qg.ERR_UNSUPPORTED
+    q_bad = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 64, 1, 0), quant_b=(qg.QUANT_BLOCK_F32, 64, 128, 0))
+    assert run(g, op=q_bad, **ok) == qg.ERR_UNSUPPORTED
+    # scale shapes: U rows = M, V rows = ceil(N / 128), both ceil(K / 128) columns
+    assert run(g, op=q, **{**ok, "Ud": qg.layout("f32", M - 1, K // 128, ld=8)}) == qg.ERR_INVALID_ARG
+    assert run(g, op=q, **{**ok, "Vd": qg.layout("f32", N // 128 + 1, K // 128, ld=8)}) == qg.ERR_INVALID_ARG
+    assert run(g, op=q, **{**ok, "Ud": qg.layout("f16", M, K // 128, ld=8)}) == qg.ERR_UNSUPPORTED
+    # scale row pitch must be 16-byte aligned
+    assert run(g, op=q, **{**ok, "Ud": qg.layout("f32", M, K // 128, ld=5)}) == qg.ERR_ALIGNMENT
+    # e4m3 A with a bf16 B
+    assert run(g, op=q, **{**ok, "Bd": qg.layout("bf16", N, K)}) == qg.ERR_UNSUPPORTED
+    # a valid request plans onto a block-scaled fp8 kernel with 128-deep k-tiles
+    d = dict(kv.split("=") for kv in g.plan(q, Ad, Ud, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["kernel"].startswith("f8_E4M3_") and d["bk"] == "128"
+    # grouped: V carries one scale matrix per expert
+    off = FAKE
+    Ag = qg.layout("e4m3", M, K, num=4, offsets=off)
+    Bg = qg.layout("e4m3", N, K, num=4, stride=N * K)
+    Dg = qg.layout("bf16", M, N, num=4, offsets=off)
+    Ug = qg.layout("f32", M, K // 128, ld=8, num=4, offsets=off)
+    Vg = qg.layout("f32", N // 128, K // 128, ld=8, num=4, stride=3 * 8)
+    d = dict(kv.split("=") for kv in g.plan(q, Ag, Ug, Bg, Vg, None, Dg, 1.0, 0.0, ws_desc()).split())
+    assert d["kernel"].startswith("f8_E4M3_") and d["schedule"] == "grouped"
+    Vshort = qg.layout("f32", N // 128, K // 128, ld=8, num=4, stride=3 * 8 - 4)
+    with pytest.raises(qg.QGemmError) as e:
+        g.plan(q, Ag, Ug, Bg, Vshort, None, Dg, 1.0, 0.0, ws_desc())
+    assert e.value.status == qg.ERR_INVALID_ARG

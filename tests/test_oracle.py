@@ -297,6 +297,28 @@ def test_fp8_quantized_matches_numpy():
         assert np.allclose(ref[off[e]:off[e + 1]], want, rtol=1e-12, atol=1e-12)
 
 
+def test_fp8_dense_ragged_matches_numpy():
+    # N and K not multiples of the 128 block: the last block of V and U is partial
+    p = synth.dense_fp8_problem(7, 300, 400, c_dtype="f32", alpha=0.5, beta=2.0, seed=3)
+    ref, _ = oracle.gemm(p)
+    dec = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    K, N = 400, 300
+    a = dec[p["A"]] * np.repeat(p["U"].astype(np.float64), 128, axis=1)[:, :K]
+    vb = np.repeat(np.repeat(p["V"].astype(np.float64), 128, axis=0), 128, axis=1)[:N, :K]
+    want = 0.5 * (a @ (dec[p["B"]] * vb).T) + 2.0 * p["C"].astype(np.float64)
+    assert p["U"].shape == (7, 4) and p["V"].shape == (3, 4)
+    assert np.allclose(ref, want, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_dense_equals_grouped_single_expert():
+    p = synth.dense_fp8_problem(9, 256, 384, seed=4)
+    ref, absdot = oracle.gemm(p)
+    q = dict(p, kind="grouped", E=1, offsets=np.array([0, 9], dtype=np.int32), counts=np.array([9]),
+             B=p["B"][None], V=p["V"][None])
+    ref_g, absdot_g = oracle.gemm(q)
+    assert np.array_equal(ref, ref_g) and np.array_equal(absdot, absdot_g)
+
+
 # ---------------------------------------------------------------- grouped
 def test_grouped_equals_per_expert_numpy():
     counts = np.array([5, 0, 17, 1, 0, 9], dtype=np.int32)
