@@ -8,9 +8,12 @@ resident in HBM before timing starts; several input sets are rotated so that
 the working set exceeds the 256 MB Infinity Cache and steps do not hit data
 left in cache by the previous step. The timed steps are captured once in a HIP
 graph and replayed, so host-side call overhead does not open gaps between
-launches. The headline `value` is TFLOP/s over the timed steps. A second workload -- the skinny decode GEMM M=16, N=4096,
-K=14336 with split-K 8 (and stream-K) -- is timed the same way and reported
-in GB/s of algorithmic bytes under "decode".
+launches. The headline `value` is TFLOP/s over the timed steps. A second
+workload -- the skinny decode GEMM M=16, N=4096, K=14336 with split-K 8 (and
+stream-K) -- is timed the same way and reported in GB/s of algorithmic bytes
+under "decode". The weight-only int4 GEMM (64 x 8192 x 8192) and the grouped
+MoE GEMM (64 experts, 65536 Zipf-distributed rows, N 2048, K 7168; bf16 and
+block-scaled fp8) are reported under "w4a16", "moe" and "moe_fp8".
 
 `roofline` describes the dominant kernel: algorithmic flops per launch over
 its mean launch time, measured with HIP events on the launch stream, against
@@ -34,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 4096 flop/clk * 2.4 GHz (dense, no sparsity)
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -61,14 +65,21 @@ def traffic_from_profile(kernel: str, workload: str):
 
 
 class Workload:
-    """Rotating device input sets for one problem and a bound qg_run call."""
+    """Rotating device input sets for one problem and a bound qg_run call.
+    With same_data, one problem is generated and uploaded `nsets` times (the
+    copies only differ in address, which is all the caches see)."""
 
-    def __init__(self, g, ws, make_problem, nsets, op):
+    def __init__(self, g, ws, make_problem, nsets, op, same_data=False):
         import torch
         import quantized_gemm_bf16_amd as qg
         from tests.gpu_util import Run
-        self.runs = [Run(g, make_problem(i), ws) for i in range(nsets)]
-        self.op = op
+        if same_data:
+            p = make_problem(0)
+            self.runs = [Run(g, p, ws) for _ in range(nsets)]
+            del p
+        else:
+            self.runs = [Run(g, make_problem(i), ws) for i in range(nsets)]
+        self.op = op if op is not None else self.runs[0].op()
         self.qg = qg
         self.torch = torch
 
@@ -129,7 +140,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["square", "decode"], default=None, help="time one workload only (profiling)")
+    ap.add_argument("--only", choices=["square", "decode", "w4a16", "moe", "moe_fp8"], default=None,
+                    help="time one workload only (profiling)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the W4A16 and MoE workloads")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -188,6 +201,34 @@ def main():
             del dw
         out["decode"] = dict(bytes_per_call=dec_bytes, **res)
 
+    extra = not args.no_extra and args.only is None
+    if extra or args.only == "w4a16":
+        # B 33.5 MB + scales 1 MB per set: 9 sets exceed the 256 MB Infinity Cache
+        w4_bytes = 64 * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 64 * 2 + 64 * 8192 * 2
+        ww = Workload(g, ws, lambda i: synth.config_w4a16(), nsets=9, op=None, same_data=True)
+        t = ww.time(args.steps, args.warmup)
+        us = t["kernel_ms_mean"] * 1e3
+        out["w4a16"] = {"kernel_us_mean": round(us, 3), "GB/s": round(w4_bytes / (us * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(w4_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "TFLOP/s": round(2.0 * 64 * 8192 * 8192 / (us * 1e-6) / 1e12, 2),
+                        "bytes_per_call": w4_bytes, "plan": ww.runs[0].plan()}
+        del ww
+    for fp8 in (False, True):
+        name = "moe_fp8" if fp8 else "moe"
+        if not (extra or args.only == name):
+            continue
+        # one set of 2.8 GB (bf16) / 1.4 GB (fp8) is far beyond every cache
+        mw = Workload(g, ws, lambda i: synth.config_moe(fp8=fp8), nsets=1, op=None)
+        p0 = mw.runs[0].p
+        mflops = 2.0 * p0["M"] * p0["N"] * p0["K"]
+        t = mw.time(max(10, args.steps // 5), max(3, args.warmup // 5))
+        us = t["kernel_ms_mean"] * 1e3
+        peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+        out[name] = {"kernel_us_mean": round(us, 1), "TFLOP/s": round(mflops / (us * 1e-6) / 1e12, 1),
+                     "frac_peak": round(mflops / (us * 1e-6) / 1e12 / peak, 4), "peak": peak,
+                     "flops_per_call": mflops, "plan": mw.runs[0].plan()}
+        del mw, p0
+
     if args.only:
         print(json.dumps(out))
         return 0
@@ -222,6 +263,9 @@ def main():
         d = out["decode"][k]
         line["decode"][k] = {"kernel_us_mean": round(d["kernel_us_mean"], 3), "GB/s": round(d["gbs"], 1),
                              "frac_hbm": round(d["frac_hbm"], 4), "plan": d["plan"]}
+    for k in ("w4a16", "moe", "moe_fp8"):
+        if k in out:
+            line[k] = out[k]
     if not args.no_cpu:
         p = synth.config_square("bf16")
         line["cpu_baseline"] = cpu_baseline(p, 2.0 * N * K)

@@ -66,6 +66,11 @@ class QGemmError(RuntimeError):
 def _load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m quantized_gemm_bf16_amd.build`")
+    # PyTorch ships its own HIP runtime, asked for by file name (libamdhip64.so)
+    # but carrying the soname libamdhip64.so.7 that libqgemm.so asks for. Loaded
+    # first, it satisfies both; if libqgemm.so came first, torch would load a
+    # second HIP runtime into the process and the two would not share devices.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     P = ctypes.POINTER

@@ -525,7 +525,13 @@ int launch(const Plan& pl, hipStream_t s) {
   if (pl.grid <= 0) return QG_OK;
   const KernelInfo& k = kKernels[pl.c.kernel];
   hipError_t e = k.launch(pl.a, pl.grid, s);
-  return e == hipSuccess ? QG_OK : QG_ERR_HIP;
+  if (e != hipSuccess) {
+    // the status code carries no HIP detail; QG_VERBOSE=1 prints it
+    static const bool verbose = getenv("QG_VERBOSE") && atoi(getenv("QG_VERBOSE")) > 0;
+    if (verbose) fprintf(stderr, "qgemm: launch of %s failed: %s\n", k.name, hipGetErrorString(e));
+    return QG_ERR_HIP;
+  }
+  return QG_OK;
 }
 
 std::string describe(const Plan& pl) {

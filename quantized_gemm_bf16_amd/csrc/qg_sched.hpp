@@ -2,8 +2,9 @@
 //
 // A core supplies: BM, BN (output tile), NT (threads), SMEM_BYTES, an Acc
 // type holding one tile's accumulators, mainloop(a, unit, smem, acc) over the
-// unit's k-tiles, store(a, unit, acc) (epilogue), and write_partial /
-// add_partial on the partials workspace.
+// unit's k-tiles, store(a, unit, acc) (epilogue), write_partial on the
+// partials workspace and, for reading partial tiles back, the lane's NCH
+// 16-byte chunks (chunk_off, get4 / set4, holds_partial).
 //
 //   DP       one unit = one whole tile; with one workgroup per tile the block
 //            id is remapped so each XCD (own L2) gets a contiguous range.
@@ -80,6 +81,50 @@ struct Sched {
     return *flag;
   }
 
+  // tot = (...((seg_0 + seg_1) + seg_2) ...) over the ns segments of a tile,
+  // in k order, read back from the workspace (slot_of(i) = slot of segment
+  // i). Small partial tiles (NCH < 32 chunks per lane) issue the loads of RB
+  // segments together (at most 32 16-byte loads per lane) before summing any
+  // of them, so they do not pay one memory round trip per segment; the empty
+  // asm ends a round so that the compiler does not hoist the next round's
+  // loads (which would spill). Large tiles go segment by segment.
+  template <class SlotOf>
+  __device__ __forceinline__ static void reduce(const Args& a, int ns, SlotOf slot_of, Acc& tot) {
+    if (!Core::holds_partial()) return;
+    using S4 = decltype(Core::get4(tot, 0));
+    constexpr int NCH = Core::NCH;
+    if constexpr (NCH >= 32) {
+      for (int q = 0; q < ns; ++q) {
+        const auto r = Core::slot_rsrc(a, slot_of(q));
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const S4 x = __builtin_bit_cast(S4, load_sc1_x4(r, Core::chunk_off(c)));
+          Core::set4(tot, c, q == 0 ? x : Core::get4(tot, c) + x);
+        }
+      }
+    } else {
+      constexpr int RB = 32 / NCH > 8 ? 8 : 32 / NCH;
+      for (int q0 = 0; q0 < ns; q0 += RB) {
+        S4 x[RB][NCH];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const auto r = Core::slot_rsrc(a, slot_of(min(q0 + j, ns - 1)));
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) x[j][c] = __builtin_bit_cast(S4, load_sc1_x4(r, Core::chunk_off(c)));
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          S4 t = Core::get4(tot, c);
+#pragma unroll
+          for (int j = 0; j < RB; ++j)
+            if (q0 + j < ns) t = (q0 + j == 0) ? x[j][c] : t + x[j][c];
+          Core::set4(tot, c, t);
+        }
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+
   __device__ __forceinline__ static void finish_counter(const Args& a, const Unit& u) {
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + u.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -112,7 +157,7 @@ struct Sched {
       Core::mainloop(a, u, smem, acc);
       if (arrive(a, u, t * a.splits + s, acc, flag)) {
         const int ns = (a.iters + a.iters_per_split - 1) / a.iters_per_split;
-        for (int q = 0; q < ns; ++q) Core::add_partial(a, t * a.splits + q, acc, q == 0);
+        reduce(a, ns, [&](int q) { return t * a.splits + q; }, acc);
         Core::store(a, u, acc);
         finish_counter(a, u);
       }
@@ -144,7 +189,7 @@ struct Sched {
           if (arrive(a, u, slot, acc, flag)) {
             const int t0 = t * ipt;
             const int plo = sk_owner(a, t0), phi = sk_owner(a, t0 + ipt - 1);
-            for (int q = plo; q <= phi; ++q) Core::add_partial(a, 2 * q + (sk_start(a, q) >= t0 ? 0 : 1), acc, q == plo);
+            reduce(a, phi - plo + 1, [&](int i) { return 2 * (plo + i) + (sk_start(a, plo + i) >= t0 ? 0 : 1); }, acc);
             Core::store(a, u, acc);
             finish_counter(a, u);
           }

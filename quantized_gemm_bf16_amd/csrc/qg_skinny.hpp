@@ -236,17 +236,12 @@ struct Skinny {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) store_sc1_x4(r, pofs(tn, mt), __builtin_bit_cast(i32x4, acc.v[tn][mt]));
   }
-  __device__ __forceinline__ static void add_partial(const Args& a, int slot, Acc& tot, bool first) {
-    if (!Cfg::NSPLIT && wave_id() != 0) return;
-    const auto r = slot_rsrc(a, slot);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const S4 x = __builtin_bit_cast(S4, load_sc1_x4(r, pofs(tn, mt)));
-        tot.v[tn][mt] = first ? x : tot.v[tn][mt] + x;
-      }
-  }
+  // Chunk c = tn * MT + mt of a lane's partial tile.
+  static constexpr int NCH = TN * MT;
+  __device__ __forceinline__ static bool holds_partial() { return Cfg::NSPLIT || wave_id() == 0; }
+  __device__ __forceinline__ static uint32_t chunk_off(int c) { return pofs(c / MT, c % MT); }
+  __device__ __forceinline__ static S4 get4(const Acc& acc, int c) { return acc.v[c / MT][c % MT]; }
+  __device__ __forceinline__ static void set4(Acc& acc, int c, const S4& x) { acc.v[c / MT][c % MT] = x; }
 };
 
 template <class Cfg>

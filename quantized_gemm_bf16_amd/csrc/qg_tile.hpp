@@ -349,23 +349,22 @@ struct Tile {
         }
   }
 
-  // tot = (...((seg_0 + seg_1) + seg_2) ...) in k order, read back from the workspace.
-  __device__ __forceinline__ static void add_partial(const Args& a, int slot, Acc& tot, bool first) {
-    const auto r = slot_rsrc(a, slot);
-    const uint32_t base = (uint32_t)((wave_id() * NQ * 64 + lane_id()) * 16);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q = (tn * TM + tm) * 4 + g;
-          const S4 x = __builtin_bit_cast(S4, load_sc1_x4(r, base + q * 1024));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) tot.v[tn][tm][4 * g + j] = first ? x[j] : tot.v[tn][tm][4 * g + j] + x[j];
-        }
+  // Chunk c = (tn * TM + tm) * 4 + g of a lane's partial tile: accumulator
+  // elements 4g .. 4g+3 of block (tn, tm), stored at base + 1024 c.
+  static constexpr int NCH = NQ;
+  __device__ __forceinline__ static bool holds_partial() { return true; }
+  __device__ __forceinline__ static uint32_t chunk_off(int c) {
+    return (uint32_t)((wave_id() * NQ * 64 + lane_id()) * 16 + c * 1024);
   }
-
+  __device__ __forceinline__ static S4 get4(const Acc& acc, int c) {
+    const int tn = c / (TM * 4), tm = (c / 4) % TM, g = c % 4;
+    return S4{acc.v[tn][tm][4 * g], acc.v[tn][tm][4 * g + 1], acc.v[tn][tm][4 * g + 2], acc.v[tn][tm][4 * g + 3]};
+  }
+  __device__ __forceinline__ static void set4(Acc& acc, int c, const S4& x) {
+    const int tn = c / (TM * 4), tm = (c / 4) % TM, g = c % 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc.v[tn][tm][4 * g + j] = x[j];
+  }
 };
 
 }  // namespace qg
