@@ -33,14 +33,14 @@ struct SkinnyCfg {
   static constexpr int BNW = NSPLIT ? BN / NW : BN;  // columns per wave
   static constexpr int NT = NW * 64, BM = 16 * MT, TN = BNW / 16;
   static constexpr int ESIZE = (E_ == El::BF16 || E_ == El::F16) ? 2 : 1;
-  static constexpr int BLKB = BLKB_;              // bytes of k per row per block (256 or 512)
+  static constexpr int BLKB = BLKB_;              // bytes of k per row per block (256, 512 or 1024)
   static constexpr int CPR = BLKB / 16;           // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;            // rows filled by one 64-lane load
   static constexpr int STEPS = BLKB / 64;         // MFMA k-steps per block
   static constexpr int BK = BLKB / ESIZE;         // k elements per block
   static constexpr int SLOT = (BNW + BM) * BLKB;  // LDS bytes of one wave's ring slot
   static constexpr int LPS = (BNW + BM) / RPI;    // 64-lane loads per slot
-  static_assert(BLKB == 256 || BLKB == 512, "block bytes");
+  static_assert(BLKB == 256 || BLKB == 512 || BLKB == 1024, "block bytes");
   static_assert(NW * DEPTH * SLOT <= 160 * 1024 - 4096, "LDS budget");
   static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
   static constexpr bool INT = (E_ == El::I8);

@@ -163,6 +163,22 @@ __device__ __forceinline__ void epi_store4(const Args& a, int64_t m, int n, cons
       if (n + j < a.N) p[j] = v[j];
 }
 
+// Scheduling hint: spread NR LDS reads over the next NM MFMAs (PER reads after
+// each MFMA) so that the reads of the next k-step's fragments overlap the
+// current k-step's MFMAs instead of being issued after them.
+template <int NR, int NM, int PER>
+struct Interleave {
+  __device__ __forceinline__ static void emit() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR < PER ? NR : PER, 0);
+    if constexpr (NM > 1) Interleave<(NR > PER ? NR - PER : 0), NM - 1, PER>::emit();
+  }
+};
+template <int NR, int NM>
+__device__ __forceinline__ void interleave_reads() {
+  Interleave<NR, NM, (NR + NM - 1) / NM>::emit();
+}
+
 // ---- the kernel body -----------------------------------------------------
 template <class Cfg>
 struct Tile {
@@ -287,6 +303,7 @@ struct Tile {
         if (ks + 1 < KS) {
           read_frags(st, ks + 1, nxt);
           mma(cur, 0, TN);
+          interleave_reads<(TM + TN) * Cfg::CH, TM * TN>();
         } else {
           // Last k-step of this stage: its fragments are already in registers.
           // Half of its MFMAs cover the wait for the next stage; after the
@@ -299,6 +316,7 @@ struct Tile {
           issue(st, u.kb + it + S);
           read_frags((it + 1) % S, 0, nxt);
           mma(cur, TN / 2, TN);
+          interleave_reads<(TM + TN) * Cfg::CH, TM * (TN - TN / 2)>();
         }
         cur = nxt;
       }
