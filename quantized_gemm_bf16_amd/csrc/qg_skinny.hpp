@@ -64,9 +64,32 @@ struct Skinny {
   static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BNW = Cfg::BNW;
   static constexpr int SMEM_BYTES = NW * DEPTH * Cfg::SLOT;  // per-wave rings (reused for the reduction)
   static_assert(NW * TN * MT * 64 * 16 <= SMEM_BYTES, "reduction space");
+  // v: accumulators; c: this lane's C values, loaded when the unit starts so
+  // that the epilogue does not wait for them at the end of the stream
   struct Acc {
     S4 v[TN][MT];
+    f32x4 c[TN][MT];
   };
+
+  __device__ __forceinline__ static bool stores(int w) { return Cfg::NSPLIT || w == 0; }
+
+  __device__ __forceinline__ static void prefetch_c(const Args& a, const Unit& u, Acc& acc) {
+    if constexpr (!Cfg::INT) {
+      const int w = wave_id(), l = lane_id();
+      const bool need = a.c_type >= 0 && a.beta != 0.f && stores(w);
+      const int nw0 = Cfg::NSPLIT ? w * BNW : 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int m = u.m0 + mt * 16 + (l & 15);
+          const int n = u.n0 + nw0 + tn * 16 + 4 * (l >> 4);
+          float c[4] = {0.f, 0.f, 0.f, 0.f};
+          if (need && m < u.m_end && n < a.N) load_c4(a, m, n, c);
+          acc.c[tn][mt] = f32x4{c[0], c[1], c[2], c[3]};
+        }
+    }
+  }
 
   __device__ __forceinline__ static S4 mma(i32x4 b, i32x4 a, S4 c) {
     if constexpr (Cfg::E == El::BF16) return mfma16_bf16(b, a, c);
@@ -155,6 +178,7 @@ struct Skinny {
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = S4{};
+    prefetch_c(a, u, acc);
 
     const int nk = u.ke - u.kb;
     // This wave's blocks are kb + w, kb + w + NW, ...; the count is rounded up
@@ -215,7 +239,11 @@ struct Skinny {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int n = u.n0 + nw0 + tn * 16 + 4 * (l >> 4);
-        if (n < a.N) epi_store4(a, m, n, acc.v[tn][mt]);
+        if (n >= a.N) continue;
+        if constexpr (Cfg::INT)
+          epi_store4(a, m, n, acc.v[tn][mt]);
+        else
+          epi_store4c(a, m, n, acc.v[tn][mt], acc.c[tn][mt]);
       }
     }
   }

@@ -137,14 +137,18 @@ __device__ __forceinline__ void store_d4(const Args& a, int64_t m, int n, const 
   }
 }
 
-__device__ __forceinline__ void epi_store4(const Args& a, int64_t m, int n, const f32x4& acc) {
+// D = alpha * acc (+ beta * c, c already loaded) -> D
+__device__ __forceinline__ void epi_store4c(const Args& a, int64_t m, int n, const f32x4& acc, const f32x4& c) {
   float v[4] = {a.alpha * acc[0], a.alpha * acc[1], a.alpha * acc[2], a.alpha * acc[3]};
-  if (a.c_type >= 0 && a.beta != 0.f) {
-    float c[4];
-    load_c4(a, m, n, c);
+  if (a.c_type >= 0 && a.beta != 0.f)
     for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(a.beta, c[j], v[j]);
-  }
   store_d4(a, m, n, v);
+}
+
+__device__ __forceinline__ void epi_store4(const Args& a, int64_t m, int n, const f32x4& acc) {
+  float c[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.c_type >= 0 && a.beta != 0.f) load_c4(a, m, n, c);
+  epi_store4c(a, m, n, acc, f32x4{c[0], c[1], c[2], c[3]});
 }
 
 // int8 path: D = acc (+ C when beta == 1), exact int32.
