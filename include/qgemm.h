@@ -84,11 +84,18 @@ typedef enum qg_order { QG_ROW_MAJOR = 0, QG_COL_MAJOR = 1 } qg_order;
  *                For a grouped problem rows of A/C/D/U is the total row count
  *                and B/V give ONE group's shape.
  *   ld           leading dimension (elements; uint32 words for QG_U4).
- *   num          number of groups (MoE experts); 0 or 1 = plain GEMM.
+ *   num          number of groups (MoE experts) or batches; 0 or 1 = plain GEMM.
  *   offsets      grouped A/C/D/U: DEVICE int32 array of num+1 row offsets,
  *                offsets[0] = 0, non-decreasing, offsets[num] <= rows; group e
  *                owns rows [offsets[e], offsets[e+1]). May be empty groups.
- *   stride       grouped B/V: elements (words) from group e to group e+1. */
+ *                NULL with num > 1 on A: a BATCHED problem (the batched
+ *                variant of the TileLang tutorial "gemm_variants.py",
+ *                gemm_batched): num batches of the same M x N x K shape; rows
+ *                of A/C/D/U then give ONE batch and every operand carries num.
+ *   stride       grouped / batched B/V: elements (words) from group e to group
+ *                e+1, or 0 when all groups share one B (V). Batched A/C/D/U:
+ *                must be rows * ld (batches stored back to back), else
+ *                QG_ERR_UNSUPPORTED. */
 typedef struct qg_layout {
   int32_t type;
   int32_t order;
@@ -174,7 +181,8 @@ size_t qg_partials_size(void);
  *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128)
  *   A, B e4m3 + U, V fp32 (QG_QUANT_BLOCK_F32 on both; A 1 x 128, B 128 x 128)
  *   A, B int8 -> D int32, C int32; alpha must be 1 and beta 0 or 1 (exact)
- *   any of these grouped over experts (Adesc.num = Bdesc.num = E, offsets).
+ *   any of these grouped over experts (Adesc.num = Bdesc.num = E, offsets),
+ *   and all but int4 batched (num = batch count on every operand, no offsets).
  * Returns QG_ERR_* without launching on any invalid or unsupported request. */
 int qg_run(qg_handle* h, const qg_operation* op, float alpha,
            const void* A, const qg_layout* Adesc,

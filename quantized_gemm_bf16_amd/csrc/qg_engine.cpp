@@ -74,7 +74,8 @@ struct Problem {
   int ta = -1, tb = -1, tc = -1, td = -1;
   int qa = QG_QUANT_NONE, qb = QG_QUANT_NONE;
   int64_t M = 0, N = 0, K = 0;
-  int E = 0;  // > 0: grouped
+  int E = 0;  // > 0: grouped (offsets) or batched (E batches of M rows)
+  bool batched = false;
   const void *A = nullptr, *B = nullptr, *C = nullptr, *U = nullptr, *V = nullptr;
   void* D = nullptr;
   int64_t lda = 0, ldb = 0, ldc = 0, ldd = 0, ldu = 0, ldv = 0, b_batch = 0, v_batch = 0;
@@ -84,8 +85,8 @@ struct Problem {
 
   std::string key() const {
     char buf[160];
-    snprintf(buf, sizeof buf, "%s.%s.%s.%s.q%d%d.e%d.n%lld.k%lld", dt_name(ta), dt_name(tb), tc < 0 ? "-" : dt_name(tc),
-             dt_name(td), qa, qb, E, (long long)N, (long long)K);
+    snprintf(buf, sizeof buf, "%s.%s.%s.%s.q%d%d.e%d%s.n%lld.k%lld", dt_name(ta), dt_name(tb), tc < 0 ? "-" : dt_name(tc),
+             dt_name(td), qa, qb, E, batched ? "b" : "", (long long)N, (long long)K);
     return std::string(buf);
   }
 };
@@ -108,6 +109,7 @@ struct Plan {
   int grid = 0;
   size_t partials = 0, barriers = 0;
   int tiles = 0;
+  bool batched = false;
 };
 
 }  // namespace
@@ -154,16 +156,24 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   p.qb = op->quant_b.kind;
   if (Bd->cols != p.K || Dd->rows != p.M || Dd->cols != p.N) return QG_ERR_INVALID_ARG;
   if (p.M > INT32_MAX || p.N > INT32_MAX || p.K > INT32_MAX) return QG_ERR_UNSUPPORTED;
-  // grouped
+  // grouped (device offsets) or batched (num > 1 without offsets: E batches of
+  // M rows, A/C/D batches contiguous, B batches `stride` apart)
   const bool grouped = Ad->num > 1 || Bd->num > 1 || Dd->num > 1 || Ad->offsets != nullptr;
   if (grouped) {
-    if (Ad->num < 1 || Bd->num != Ad->num || !Ad->offsets) return QG_ERR_INVALID_ARG;
-    if (Dd->num != Ad->num && Dd->num > 1) return QG_ERR_INVALID_ARG;
-    if (Dd->offsets && Dd->offsets != Ad->offsets) return QG_ERR_UNSUPPORTED;
-    if (Ad->num > 1023) return QG_ERR_UNSUPPORTED;
+    if (Ad->num < 1 || Bd->num != Ad->num) return QG_ERR_INVALID_ARG;
     p.E = Ad->num;
-    p.offsets = Ad->offsets;
-    if (!aligned16(p.offsets) && (reinterpret_cast<uintptr_t>(p.offsets) & 3)) return QG_ERR_ALIGNMENT;
+    if (Ad->offsets) {
+      if (Dd->num != Ad->num && Dd->num > 1) return QG_ERR_INVALID_ARG;
+      if (Dd->offsets && Dd->offsets != Ad->offsets) return QG_ERR_UNSUPPORTED;
+      if (Ad->num > 1023) return QG_ERR_UNSUPPORTED;
+      p.offsets = Ad->offsets;
+      if (!aligned16(p.offsets) && (reinterpret_cast<uintptr_t>(p.offsets) & 3)) return QG_ERR_ALIGNMENT;
+    } else {
+      p.batched = true;
+      if (Dd->num != Ad->num || Dd->offsets) return QG_ERR_INVALID_ARG;
+      if (Ad->stride != Ad->rows * Ad->ld || Dd->stride != Dd->rows * Dd->ld) return QG_ERR_UNSUPPORTED;
+      if ((int64_t)p.E * p.M > INT32_MAX) return QG_ERR_UNSUPPORTED;
+    }
   }
   // dtype combinations
   const bool float16ish = (p.ta == QG_BF16 || p.ta == QG_F16);
@@ -207,7 +217,8 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     if (grouped) {
       if (Vd->num != Ad->num) return QG_ERR_INVALID_ARG;
       p.v_batch = Vd->stride;
-      if (p.v_batch < Vd->rows * Vd->ld) return QG_ERR_INVALID_ARG;
+      if (p.v_batch != 0 && p.v_batch < Vd->rows * Vd->ld) return QG_ERR_INVALID_ARG;
+      if (!Ad->offsets && Ud->stride != Ud->rows * Ud->ld) return QG_ERR_UNSUPPORTED;
     }
     p.U = U;
     p.V = V;
@@ -235,8 +246,8 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   if ((p.K * esize(p.ta)) % 16) return QG_ERR_ALIGNMENT;
   if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return QG_ERR_ALIGNMENT;
   if (grouped) {
-    p.b_batch = Bd->stride;
-    if (p.b_batch < p.N * p.ldb) return QG_ERR_INVALID_ARG;
+    p.b_batch = Bd->stride;  // 0: every group uses the same B
+    if (p.b_batch != 0 && p.b_batch < p.N * p.ldb) return QG_ERR_INVALID_ARG;
   }
   // C: only read when beta != 0
   p.tc = -1;
@@ -250,6 +261,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
       return QG_ERR_UNSUPPORTED;
     }
     if ((Cd->ld * esize(Cd->type)) % 16 || !aligned16(C)) return QG_ERR_ALIGNMENT;
+    if (p.batched && (Cd->num != p.E || Cd->offsets || Cd->stride != Cd->rows * Cd->ld)) return QG_ERR_UNSUPPORTED;
     p.tc = Cd->type;
     p.C = C;
     p.ldc = Cd->ld;
@@ -321,7 +333,16 @@ int make_plan(const qg_handle* h, const Problem& p, const Choice& c, const qg_wo
   if (a.iters == 0 && mode != MODE_GROUPED) mode = MODE_DP;
   pl.c.mode = mode;
   a.mode = mode;
-  if (mode == MODE_GROUPED) {
+  if (mode == MODE_GROUPED && p.batched) {
+    a.tiles_m = (int32_t)cdiv(p.M, k.bm);  // m-tiles per batch
+    const int64_t tiles = (int64_t)p.E * a.tiles_m * a.tiles_n;
+    if (tiles > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+    pl.tiles = (int)tiles;
+    pl.grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)h->cus * 4));
+    pl.c.split = 1;
+    pl.c.programs = 0;
+    pl.batched = true;
+  } else if (mode == MODE_GROUPED) {
     a.tiles_m = (int32_t)(cdiv(p.M, k.bm) + p.E);  // upper bound on the padded m-tiles
     const int64_t ub = (int64_t)a.tiles_m * a.tiles_n;
     pl.tiles = (int)std::min<int64_t>(ub, INT32_MAX);
@@ -422,8 +443,18 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, i
   Choice c;
   const int cus = h->cus;
   if (p.E > 0 && p.ta == QG_E4M3) {
-    c.kernel = kernel_by_shape(p, 128, 256);
+    c.kernel = kernel_by_shape(p, p.batched && p.M <= 64 ? 64 : 128, 256);
     c.mode = MODE_GROUPED;
+    return c;
+  }
+  if (p.batched) {
+    // per-batch shape decides the tile; skinny kernels for small M, sized so
+    // that all batches together give about one tile per compute unit
+    c.mode = MODE_GROUPED;
+    if (p.M <= 32) c.kernel = skinny_for(p, cdiv(p.N * p.E, cus));
+    if (c.kernel < 0)
+      c.kernel = kernel_by_shape(p, p.M >= 256 && p.N >= 256 ? 256 : 128, p.M >= 256 && p.N >= 256 ? 256 : 128);
+    if (c.kernel < 0) c.kernel = kernel_by_shape(p, 128, 128);
     return c;
   }
   if (p.E > 0) {
@@ -541,7 +572,7 @@ std::string describe(const Plan& pl) {
   const KernelInfo& k = kKernels[pl.c.kernel];
   snprintf(buf, sizeof buf,
            "kernel=%s schedule=%s split=%d programs=%d tiles=%d grid=%d partials=%zu barriers=%zu bm=%d bn=%d bk=%d",
-           k.name, sched_name(pl.c.mode), pl.c.split, pl.c.programs, pl.tiles, pl.grid, pl.partials, pl.barriers, k.bm,
+           k.name, pl.batched ? "batched" : sched_name(pl.c.mode), pl.c.split, pl.c.programs, pl.tiles, pl.grid, pl.partials, pl.barriers, k.bm,
            k.bn, k.bk);
   return std::string(buf);
 }

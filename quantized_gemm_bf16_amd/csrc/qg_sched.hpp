@@ -17,6 +17,9 @@
 //   GROUPED  persistent loop over the tiles of all experts, found from the
 //            device offsets array (tutorial function gemm_grouped: padded
 //            per-expert m-block prefix; rows past an expert's end masked).
+//            Without an offsets array the groups are E batches of M rows each
+//            (tutorial function gemm_batched: the (batch, m-block, n-block)
+//            triple flattened into one tile id).
 // Split segments write fp32/int32 partial tiles to the partials workspace and
 // bump the tile's arrival counter by their k-iteration count. The segment
 // that completes the count sums all segments of the tile in k order (so the
@@ -209,34 +212,47 @@ struct Sched {
   }
 
   // Grouped: per-expert m-tile prefix built in LDS from the device offsets.
+  // Batched (a.offsets == nullptr): E batches of a.M rows, batch e owning rows
+  // [e*M, (e+1)*M) of A, C and D; a.tiles_m m-tiles per batch.
   __device__ __forceinline__ static void run_grouped(const Args& a, char* smem, int* pref) {
-    // pref[0..E] = prefix of ceil(rows_e / BM); E <= 1023 (host checked)
-    if (threadIdx.x == 0) {
-      int acc = 0;
-      pref[0] = 0;
-      for (int e = 0; e < a.E; ++e) {
-        const int rows = a.offsets[e + 1] - a.offsets[e];
-        acc += rows > 0 ? (rows + Core::BM - 1) / Core::BM : 0;
-        pref[e + 1] = acc;
+    const bool batched = a.offsets == nullptr;
+    if (!batched) {
+      // pref[0..E] = prefix of ceil(rows_e / BM); E <= 1023 (host checked)
+      if (threadIdx.x == 0) {
+        int acc = 0;
+        pref[0] = 0;
+        for (int e = 0; e < a.E; ++e) {
+          const int rows = a.offsets[e + 1] - a.offsets[e];
+          acc += rows > 0 ? (rows + Core::BM - 1) / Core::BM : 0;
+          pref[e + 1] = acc;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
-    const int total = pref[a.E] * a.tiles_n;
+    const int mtiles = batched ? a.E * a.tiles_m : pref[a.E];
+    const int total = mtiles * a.tiles_n;
     for (int b = blockIdx.x; b < total; b += gridDim.x) {
       const int mt = b / a.tiles_n, tn = b - mt * a.tiles_n;
-      int lo = 0, hi = a.E - 1;  // largest e with pref[e] <= mt
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pref[mid] <= mt)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
       Unit u;
-      u.expert = lo;
+      if (batched) {
+        const int e = mt / a.tiles_m;
+        u.expert = e;
+        u.m0 = e * a.M + (mt - e * a.tiles_m) * Core::BM;
+        u.m_end = (e + 1) * a.M;
+      } else {
+        int lo = 0, hi = a.E - 1;  // largest e with pref[e] <= mt
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pref[mid] <= mt)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        u.expert = lo;
+        u.m0 = a.offsets[lo] + (mt - pref[lo]) * Core::BM;
+        u.m_end = a.offsets[lo + 1];
+      }
       u.tile = b;
-      u.m0 = a.offsets[lo] + (mt - pref[lo]) * Core::BM;
-      u.m_end = a.offsets[lo + 1];
       u.n0 = tn * Core::BN;
       u.kb = 0;
       u.ke = a.iters;

@@ -232,6 +232,35 @@ def grouped_problem(counts, N, K, in_dtype=BF16, out_dtype=BF16, seed=SEED_A, a_
     return p
 
 
+def batched_problem(batch, M, N, K, in_dtype=BF16, out_dtype=BF16, c_dtype=None, alpha=1.0, beta=0.0,
+                    seed=SEED_A, share_b=False, fp8=False, a_std=1.0, b_std=0.02):
+    """Batched GEMM: `batch` products of the same M x N x K shape. Stored as a
+    grouped problem with `batch` groups of M rows (A [batch*M, K], B [batch, N, K],
+    C/D [batch*M, N]) and flagged `batched`; share_b: every batch uses B[0]."""
+    counts = np.full(batch, M, dtype=np.int32)
+    if in_dtype == I8:
+        p = dict(kind="grouped", M=batch * M, N=N, K=K, E=batch, counts=counts,
+                 offsets=offsets_from_counts(counts), in_dtype=I8, out_dtype=I32, c_dtype=None,
+                 alpha=1.0, beta=0.0, A=int8_uniform((batch * M, K), seed),
+                 B=int8_uniform((batch, N, K), seed + 1))
+        if c_dtype is not None:
+            p["C"] = rng(seed + 2).integers(-(1 << 20), 1 << 20, size=(batch * M, N), dtype=np.int64).astype(np.int32)
+            p.update(c_dtype=I32, beta=float(beta))
+    else:
+        p = grouped_problem(counts, N, K, in_dtype=in_dtype, out_dtype=out_dtype, seed=seed, a_std=a_std,
+                            b_std=b_std, fp8=fp8)
+        p.update(alpha=float(alpha), beta=float(beta))
+        if c_dtype is not None:
+            p["C"] = to_storage(normal((batch * M, N), 1.0, seed + 2), c_dtype)
+            p["c_dtype"] = c_dtype
+    if share_b:
+        p["B"] = np.ascontiguousarray(np.broadcast_to(p["B"][:1], p["B"].shape))
+        if fp8:
+            p["V"] = np.ascontiguousarray(np.broadcast_to(p["V"][:1], p["V"].shape))
+    p.update(batched=True, share_b=share_b, batch_M=M)
+    return p
+
+
 # ---------------------------------------------------------------------------
 # the five workloads the engine is measured and checked on
 # ---------------------------------------------------------------------------

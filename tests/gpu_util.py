@@ -75,7 +75,16 @@ class Run:
         self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") if self.out != "i32" \
             else torch.full((M, self.ldn), -7, dtype=torch.int32, device="cuda")
         kind = p["kind"]
-        if kind == "grouped":
+        if p.get("batched"):
+            # batched: every descriptor gives ONE batch; A/C/D batches back to back
+            E, Mb = p["E"], p["batch_M"]
+            nb = 1 if p.get("share_b") else E
+            if p.get("share_b"):
+                self.B = dev(p["B"][0])
+            self.Ad = qg.layout(p["in_dtype"], Mb, K, num=E, stride=Mb * K)
+            self.Bd = qg.layout(p["in_dtype"], N, K, num=E, stride=0 if nb == 1 else N * K)
+            self.Dd = qg.layout(self.out, Mb, N, ld=self.ldn, num=E, stride=Mb * self.ldn)
+        elif kind == "grouped":
             E = p["E"]
             self.off = dev(np.asarray(p["offsets"], dtype=np.int32))
             self.Ad = qg.layout(p["in_dtype"], M, K, num=E, offsets=self.off.data_ptr())
@@ -87,10 +96,19 @@ class Run:
             self.Bd = qg.layout(bt, N, K)
             self.Dd = qg.layout(self.out, M, N, ld=self.ldn)
         self.Cd = qg.layout(p["c_dtype"], M, N, ld=self.ldn) if self.C is not None else None
+        if p.get("batched") and self.C is not None:
+            self.Cd = qg.layout(p["c_dtype"], p["batch_M"], N, ld=self.ldn, num=p["E"], stride=p["batch_M"] * self.ldn)
         self.Ud = self.Vd = None
         if kind == "w4a16":
             self.Vd = qg.layout("f16", N, p["V"].shape[1], ld=self.ldv)
-        if p.get("U") is not None and kind == "grouped":
+        if p.get("U") is not None and p.get("batched"):
+            nb, kg = p["V"].shape[1], p["V"].shape[2]
+            Mb = p["batch_M"]
+            if p.get("share_b"):
+                self.V = self.V[:1].contiguous()
+            self.Ud = qg.layout("f32", Mb, p["U"].shape[1], ld=self.ldu, num=p["E"], stride=Mb * self.ldu)
+            self.Vd = qg.layout("f32", nb, kg, ld=self.ldv, num=p["E"], stride=0 if p.get("share_b") else nb * self.ldv)
+        elif p.get("U") is not None and kind == "grouped":
             nb, kg = p["V"].shape[1], p["V"].shape[2]
             self.Ud = qg.layout("f32", M, p["U"].shape[1], ld=self.ldu, num=p["E"], offsets=self.off.data_ptr())
             self.Vd = qg.layout("f32", nb, kg, ld=self.ldv, num=p["E"], stride=nb * self.ldv)

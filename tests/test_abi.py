@@ -274,3 +274,26 @@ def test_fp8_block_scaled_validation(g):
     with pytest.raises(qg.QGemmError) as e:
         g.plan(q, Ag, Ug, Bg, Vshort, None, Dg, 1.0, 0.0, ws_desc())
     assert e.value.status == qg.ERR_INVALID_ARG
+
+
+def test_batched_validation_and_plan(g):
+    E, M, N, K = 4, 100, 256, 512
+    Ad = qg.layout("bf16", M, K, num=E, stride=M * K)
+    Bd = qg.layout("bf16", N, K, num=E, stride=N * K)
+    Dd = qg.layout("bf16", M, N, num=E, stride=M * N)
+    d = dict(kv.split("=") for kv in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["schedule"] == "batched" and int(d["tiles"]) > 0
+    # one shared B (stride 0) is accepted
+    g.plan(qg.operation(), Ad, None, qg.layout("bf16", N, K, num=E, stride=0), None, None, Dd, 1.0, 0.0, ws_desc())
+    # batch counts must agree; A/C/D batches must be back to back
+    assert run(g, Ad=Ad, Bd=qg.layout("bf16", N, K, num=E - 1, stride=N * K), Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, Ad=Ad, Bd=Bd, Dd=qg.layout("bf16", M, N, num=E - 1, stride=M * N)) == qg.ERR_INVALID_ARG
+    assert run(g, Ad=qg.layout("bf16", M, K, num=E, stride=M * K + 8), Bd=Bd, Dd=Dd) == qg.ERR_UNSUPPORTED
+    assert run(g, Ad=Ad, Bd=Bd, Dd=Dd, beta=1.0, C=FAKE, Cd=qg.layout("bf16", M, N, num=E, stride=M * N + 8)) == \
+        qg.ERR_UNSUPPORTED
+    # B stride shorter than one B
+    assert run(g, Ad=Ad, Bd=qg.layout("bf16", N, K, num=E, stride=N * K - 8), Dd=Dd) == qg.ERR_INVALID_ARG
+    # the int4 path is not batched
+    q = qg.operation(quant_b=(qg.QUANT_INT4_ZP, 128, 1, 8))
+    assert run(g, op=q, Ad=Ad, Bd=qg.layout("u4", N, K, num=E, stride=N * K // 8), Dd=Dd, V=FAKE,
+               Vd=qg.layout("f16", N, K // 128, num=E, stride=N * K // 128)) == qg.ERR_UNSUPPORTED

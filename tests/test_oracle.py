@@ -389,3 +389,17 @@ def test_zipf_counts_properties():
 def test_pack_int4_layout_literal():
     q = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 15, 0, 0, 0, 0, 0, 0, 9]], dtype=np.int64)
     assert synth.pack_int4(q).tolist() == [[0x87654321, 0x9000000F]]
+
+
+def test_batched_problem_matches_numpy_per_batch():
+    # the batched generator goes through the oracle's grouped definition
+    p = synth.batched_problem(3, 5, 40, 48, c_dtype="f32", alpha=0.5, beta=2.0, seed=21, share_b=True)
+    ref, _ = oracle.gemm(p)
+    a = _bf16_to_f64(p["A"])
+    b = _bf16_to_f64(p["B"][0])
+    c = p["C"].astype(np.float64)
+    for e in range(3):
+        rows = slice(5 * e, 5 * e + 5)
+        want = 0.5 * (a[rows] @ b.T) + 2.0 * c[rows]
+        assert np.allclose(ref[rows], want, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(p["B"][1], p["B"][0]) and np.array_equal(p["B"][2], p["B"][0])
