@@ -117,7 +117,36 @@ typedef enum qg_policy {
   QG_POLICY_FORCE = 3    /* use schedule / split_k / programs / kernel exactly as given */
 } qg_policy;
 
-typedef enum qg_epilogue { QG_EPI_ALPHA_BETA = 0 } qg_epilogue;
+/* Epilogue, applied to each output element once its sum is complete (the
+ * fused GEMM + bias + activation and the fused output quantisation of the
+ * DeepGEMM write-up, section 6). Flags combine; the steps run in this order:
+ *   x = alpha * acc + beta * C[m, n]              (always)
+ *   x = x + bias[n]                               QG_EPI_BIAS
+ *   x = max(x, 0)                                 QG_EPI_RELU
+ *   x = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))  QG_EPI_GELU (exact erf form)
+ *   D[m, n] = saturate_int8(round_half_even(x * row_scale[m] + zero_point))
+ *                                                 QG_EPI_QUANT_I8 (D type QG_I8)
+ * otherwise D[m, n] = x rounded (RNE) to D's type. RELU and GELU exclude each
+ * other. The int8-input path (exact int32 results) takes no epilogue flags. */
+typedef enum qg_epilogue {
+  QG_EPI_ALPHA_BETA = 0,
+  QG_EPI_BIAS = 1,
+  QG_EPI_RELU = 2,
+  QG_EPI_GELU = 4,
+  QG_EPI_QUANT_I8 = 8
+} qg_epilogue;
+
+/* Operands of the epilogue flags (ignored when the flag is not set). */
+typedef struct qg_epilogue_args {
+  const void* bias;        /* DEVICE, N elements of bias_type (QG_F32, QG_BF16 or
+                              QG_F16), one per column of D, 16-byte aligned */
+  int32_t bias_type;
+  int32_t reserved0;
+  const float* row_scale;  /* DEVICE, one fp32 scale per row of D (grouped /
+                              batched: per row of the whole A), 4-byte aligned */
+  float zero_point;        /* added after scaling, before rounding */
+  int32_t reserved1;
+} qg_epilogue_args;
 
 typedef enum qg_quant_kind {
   QG_QUANT_NONE = 0,
@@ -141,13 +170,14 @@ typedef enum qg_schedule {
 
 typedef struct qg_operation {
   int32_t policy;    /* qg_policy */
-  int32_t epilogue;  /* qg_epilogue */
+  int32_t epilogue;  /* qg_epilogue flags */
   qg_quant quant_a;
   qg_quant quant_b;
   int32_t schedule;  /* qg_schedule (honoured under FORCE; a hint otherwise) */
   int32_t split_k;   /* SPLITK chunk count, 0 = engine's choice */
   int32_t programs;  /* STREAMK program count, 0 = number of compute units */
   int32_t kernel;    /* FORCE: registry index from qg_kernel_name, -1 = engine's choice */
+  qg_epilogue_args epi;
 } qg_operation;
 
 /* Caller-owned workspace. `barriers` holds one int32 arrival counter per
@@ -181,6 +211,7 @@ size_t qg_partials_size(void);
  *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128)
  *   A, B e4m3 + U, V fp32 (QG_QUANT_BLOCK_F32 on both; A 1 x 128, B 128 x 128)
  *   A, B int8 -> D int32, C int32; alpha must be 1 and beta 0 or 1 (exact)
+ *   float paths with QG_EPI_QUANT_I8 -> D int8
  *   any of these grouped over experts (Adesc.num = Bdesc.num = E, offsets),
  *   and all but int4 batched (num = batch count on every operand, no offsets).
  * Returns QG_ERR_* without launching on any invalid or unsupported request. */

@@ -52,6 +52,9 @@ class _Problem(ctypes.Structure):
         ("E", ctypes.c_int32), ("offsets", ctypes.c_void_p),
         ("b_batch", ctypes.c_int64), ("v_batch", ctypes.c_int64),
         ("splits", ctypes.c_int32),
+        ("epi", ctypes.c_int32), ("bias_type", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
+        ("out_zero_point", ctypes.c_double),
     ]
 
 
@@ -82,6 +85,9 @@ def lib():
             f.argtypes = [at]
             f.restype = ctypes.c_double
         L.or_num_threads.restype = ctypes.c_int
+        L.or_quant_codes.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.or_quant_codes.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -106,12 +112,9 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def gemm(p: dict, rows=None, splits: int = 1, alpha=None, beta=None):
-    """fp64 reference for a problem dict built by `synth`.
-
-    Returns (ref, absdot), float64 arrays of shape [len(rows) or M, N].
-    `alpha` / `beta` override the problem's own values."""
-    keep = []
+def _problem(p: dict, splits: int, alpha, beta, keep):
+    """Marshals a problem dict into the C struct (arrays appended to `keep`,
+    which the caller holds while the struct is in use)."""
 
     def c(a):
         a = np.ascontiguousarray(a)
@@ -160,6 +163,34 @@ def gemm(p: dict, rows=None, splits: int = 1, alpha=None, beta=None):
             st.qa = st.qb = Q_BLOCK
             st.U, st.ldu, st.gm_a, st.gk_a = _ptr(U), U.shape[1], 1, p["group_k"]
             st.V, st.ldv, st.gn_b, st.gk_b = _ptr(V), V.shape[1], p["group_n"], p["group_k"]
+    ep = p.get("epilogue")
+    if ep:
+        st.epi = int(ep["flags"])
+        if ep.get("bias") is not None:
+            b = c(ep["bias"])
+            st.bias, st.bias_type = _ptr(b), _DT[ep["bias_type"]]
+        if ep.get("row_scale") is not None:
+            rs = c(np.asarray(ep["row_scale"], dtype=np.float32))
+            st.row_scale = _ptr(rs)
+        st.out_zero_point = float(ep.get("zero_point", 0.0))
+    return st
+
+
+def gemm(p: dict, rows=None, splits: int = 1, alpha=None, beta=None):
+    """fp64 reference for a problem dict built by `synth` (epilogue steps
+    included when p["epilogue"] is set; quantisation is quant_codes).
+
+    Returns (ref, absdot), float64 arrays of shape [len(rows) or M, N].
+    `alpha` / `beta` override the problem's own values."""
+    keep = []
+
+    def c(a):
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a
+
+    M, N = p["M"], p["N"]
+    st = _problem(p, splits, alpha, beta, keep)
     if rows is None:
         n = M
         rp = None
@@ -173,6 +204,26 @@ def gemm(p: dict, rows=None, splits: int = 1, alpha=None, beta=None):
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return ref, absdot
+
+
+def quant_codes(p: dict, ref, rows=None):
+    """Output quantisation of oracle outputs `ref` (rows as passed to gemm):
+    returns (pre, code) with pre = ref * row_scale + zero_point (fp64) and code
+    its saturated round-half-even int8 value."""
+    keep = []
+    st = _problem(p, 1, None, None, keep)
+    ref = np.ascontiguousarray(ref, dtype=np.float64)
+    if rows is None:
+        rp, n = None, p["M"]
+    else:
+        r = np.asarray(rows, dtype=np.int64)
+        keep.append(r)
+        rp, n = _ptr(r), len(r)
+    pre = np.empty_like(ref)
+    code = np.empty(ref.shape, dtype=np.int32)
+    if lib().or_quant_codes(ctypes.byref(st), rp, n, ref.ctypes.data, pre.ctypes.data, code.ctypes.data) != 0:
+        raise ValueError("oracle rejected the problem")
+    return pre, code
 
 
 # ---------------------------------------------------------------------------

@@ -34,6 +34,14 @@
  * Grouped (MoE) problems: row r of A and D belongs to the expert e with
  * offsets[e] <= r < offsets[e+1], and uses B_e (and V_e).
  *
+ * Epilogue (the fused GEMM + bias + activation and the fused output
+ * quantisation of the DeepGEMM write-up, section 6), applied to ref in fp64:
+ *   bias (flag 1):  ref += bias(j)
+ *   ReLU (flag 2):  ref  = max(ref, 0)
+ *   GELU (flag 4):  ref  = ref * Phi(ref) = 0.5 ref (1 + erf(ref / sqrt 2))
+ *   quantisation (flag 8), or_quant_codes: t = ref * row_scale(i) + zero_point,
+ *                   code = min(max(round_half_even(t), -128), 127)
+ *
  * Split mode (self-check only): the K range is cut into `splits` contiguous
  * chunks of ceil(K/splits); each chunk is summed in fp64 on its own and the
  * chunk sums are then added in chunk order.
@@ -67,6 +75,11 @@ typedef struct {
   const int32_t* offsets;      /* E + 1 row offsets into A / D */
   int64_t b_batch, v_batch;    /* per-expert strides of B (elements or words) and V */
   int32_t splits;              /* >= 1 */
+  int32_t epi;                 /* epilogue flags: bias 1, relu 2, gelu 4, quantise 8 */
+  int32_t bias_type;           /* OR_F32 / OR_BF16 / OR_F16 */
+  const void* bias;            /* N values */
+  const float* row_scale;      /* one per row of D */
+  double out_zero_point;
 } or_problem;
 
 /* ---- scalar decoders ---------------------------------------------------- */
@@ -169,6 +182,9 @@ static void one_output(const or_problem* p, int64_t i, int64_t j, double* ref, d
   }
   double r = p->alpha * acc;
   if (p->beta != 0.0 && p->tc >= 0) r += p->beta * dec_plain(p->tc, p->C, i * p->ldc + j);
+  if (p->epi & 1) r += dec_plain(p->bias_type, p->bias, j);
+  if (p->epi & 2) r = r > 0.0 ? r : 0.0;
+  if (p->epi & 4) r = 0.5 * r * (1.0 + erf(r / sqrt(2.0)));
   *ref = r;
   *absdot = ad;
 }
@@ -185,6 +201,28 @@ int or_gemm(const or_problem* p, const int64_t* rows, int64_t nrows, double* ref
     int64_t r = t / p->N, j = t % p->N;
     int64_t i = rows ? rows[r] : r;
     one_output(p, i, j, &ref[t], &absdot[t]);
+  }
+  return 0;
+}
+
+/* Output quantisation of already computed outputs ref [nrows, N] (rows as in
+ * or_gemm): pre = ref * row_scale(i) + zero_point, code = saturated
+ * round-half-even of pre. */
+int or_quant_codes(const or_problem* p, const int64_t* rows, int64_t nrows, const double* ref, double* pre,
+                   int32_t* code) {
+  if (!p || !p->row_scale) return -1;
+  if (!rows) nrows = p->M;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t i = rows ? rows[r] : r;
+    double s = (double)p->row_scale[i];
+    for (int64_t j = 0; j < p->N; ++j) {
+      double t = ref[r * p->N + j] * s + p->out_zero_point;
+      double q = nearbyint(t); /* the default rounding mode: to nearest, ties to even */
+      if (q < -128.0) q = -128.0;
+      if (q > 127.0) q = 127.0;
+      pre[r * p->N + j] = t;
+      code[r * p->N + j] = (int32_t)q;
+    }
   }
   return 0;
 }

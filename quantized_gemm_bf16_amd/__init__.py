@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 F32, F16, BF16, E4M3, I8, I32, U4 = 0, 1, 2, 3, 4, 5, 6
 ROW_MAJOR, COL_MAJOR = 0, 1
 POLICY_DEFAULT, POLICY_MEASURE, POLICY_REUSE, POLICY_FORCE = 0, 1, 2, 3
-EPI_ALPHA_BETA = 0
+EPI_ALPHA_BETA, EPI_BIAS, EPI_RELU, EPI_GELU, EPI_QUANT_I8 = 0, 1, 2, 4, 8
 QUANT_NONE, QUANT_INT4_ZP, QUANT_BLOCK_F32 = 0, 1, 2
 SCHED_AUTO, SCHED_DP, SCHED_SPLITK, SCHED_STREAMK = 0, 1, 2, 3
 
@@ -46,10 +46,15 @@ class Quant(ctypes.Structure):
                 ("zero_point", ctypes.c_int32)]
 
 
+class EpilogueArgs(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_type", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("row_scale", ctypes.c_void_p), ("zero_point", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+
+
 class Operation(ctypes.Structure):
     _fields_ = [("policy", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("quant_a", Quant),
                 ("quant_b", Quant), ("schedule", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("programs", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+                ("programs", ctypes.c_int32), ("kernel", ctypes.c_int32), ("epi", EpilogueArgs)]
 
 
 class Workspace(ctypes.Structure):
@@ -129,8 +134,13 @@ def layout(dtype, rows, cols, ld=None, num=0, offsets=0, stride=0, order=ROW_MAJ
 
 
 def operation(policy=POLICY_DEFAULT, schedule=SCHED_AUTO, split_k=0, programs=0, kernel=-1,
-              quant_a=(QUANT_NONE, 0, 0, 0), quant_b=(QUANT_NONE, 0, 0, 0)) -> Operation:
-    return Operation(policy, EPI_ALPHA_BETA, Quant(*quant_a), Quant(*quant_b), schedule, split_k, programs, kernel)
+              quant_a=(QUANT_NONE, 0, 0, 0), quant_b=(QUANT_NONE, 0, 0, 0), epilogue=EPI_ALPHA_BETA,
+              bias=None, bias_type="f32", row_scale=None, zero_point=0.0) -> Operation:
+    """bias / row_scale: device tensors or raw pointers (kept alive by the caller)."""
+    bt = DTYPE_CODES[bias_type] if isinstance(bias_type, str) else int(bias_type)
+    epi = EpilogueArgs(_ptr(bias), bt, 0, _ptr(row_scale), float(zero_point), 0)
+    return Operation(policy, int(epilogue), Quant(*quant_a), Quant(*quant_b), schedule, split_k, programs, kernel,
+                     epi)
 
 
 def _ptr(t):

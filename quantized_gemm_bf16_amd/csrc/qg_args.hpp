@@ -6,6 +6,8 @@ namespace qg {
 
 enum Mode : int32_t { MODE_DP = 0, MODE_SPLITK = 1, MODE_STREAMK = 2, MODE_GROUPED = 3 };
 
+enum EpiFlag : int32_t { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4, EPI_QUANT_I8 = 8 };
+
 enum DType : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_I8 = 4, DT_I32 = 5, DT_U4 = 6 };
 
 struct Args {
@@ -26,6 +28,13 @@ struct Args {
   int32_t d_type;                        // DType of D
   int32_t zero_point;                    // int4
   int32_t group_k;                       // int4 scale group along K
+
+  // epilogue (flags as in the C ABI's qg_epilogue)
+  int32_t epi;
+  int32_t bias_type;
+  const void* bias;                      // N values, or null
+  const float* row_scale;                // output quantisation: one per row of D
+  float out_zero_point;
 
   // work division
   int32_t mode;

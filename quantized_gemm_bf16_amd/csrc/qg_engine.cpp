@@ -82,11 +82,15 @@ struct Problem {
   const int32_t* offsets = nullptr;
   float alpha = 1.f, beta = 0.f;
   int zp = 8, group_k = 128;
+  int epi = 0, bias_type = -1;
+  const void* bias = nullptr;
+  const float* row_scale = nullptr;
+  float out_zp = 0.f;
 
   std::string key() const {
     char buf[160];
-    snprintf(buf, sizeof buf, "%s.%s.%s.%s.q%d%d.e%d%s.n%lld.k%lld", dt_name(ta), dt_name(tb), tc < 0 ? "-" : dt_name(tc),
-             dt_name(td), qa, qb, E, batched ? "b" : "", (long long)N, (long long)K);
+    snprintf(buf, sizeof buf, "%s.%s.%s.%s.q%d%d.e%d%s.x%d.n%lld.k%lld", dt_name(ta), dt_name(tb),
+             tc < 0 ? "-" : dt_name(tc), dt_name(td), qa, qb, E, batched ? "b" : "", epi, (long long)N, (long long)K);
     return std::string(buf);
   }
 };
@@ -142,7 +146,28 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   if (!op || !Ad || !Bd || !Dd) return QG_ERR_INVALID_ARG;
   int st;
   if ((st = check_layout(Ad)) || (st = check_layout(Bd)) || (st = check_layout(Dd))) return st;
-  if (op->epilogue != QG_EPI_ALPHA_BETA) return QG_ERR_UNSUPPORTED;
+  // epilogue flags and their operands
+  {
+    const int e = op->epilogue;
+    if (e & ~(QG_EPI_BIAS | QG_EPI_RELU | QG_EPI_GELU | QG_EPI_QUANT_I8)) return QG_ERR_INVALID_ARG;
+    if ((e & QG_EPI_RELU) && (e & QG_EPI_GELU)) return QG_ERR_INVALID_ARG;
+    p.epi = e;
+    if (e & QG_EPI_BIAS) {
+      const int bt = op->epi.bias_type;
+      if (!(bt == QG_F32 || bt == QG_BF16 || bt == QG_F16)) return QG_ERR_UNSUPPORTED;
+      if (!op->epi.bias) return QG_ERR_INVALID_ARG;
+      if (!aligned16(op->epi.bias)) return QG_ERR_ALIGNMENT;
+      p.bias = op->epi.bias;
+      p.bias_type = bt;
+    }
+    if (e & QG_EPI_QUANT_I8) {
+      if (!op->epi.row_scale) return QG_ERR_INVALID_ARG;
+      if (reinterpret_cast<uintptr_t>(op->epi.row_scale) & 3) return QG_ERR_ALIGNMENT;
+      if (!std::isfinite(op->epi.zero_point)) return QG_ERR_INVALID_ARG;
+      p.row_scale = op->epi.row_scale;
+      p.out_zp = op->epi.zero_point;
+    }
+  }
   if (!std::isfinite(alpha) || !std::isfinite(beta)) return QG_ERR_INVALID_ARG;
   p.alpha = alpha;
   p.beta = beta;
@@ -178,7 +203,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   // dtype combinations
   const bool float16ish = (p.ta == QG_BF16 || p.ta == QG_F16);
   if (p.ta == QG_I8) {
-    if (p.tb != QG_I8 || p.td != QG_I32 || p.qa || p.qb) return QG_ERR_UNSUPPORTED;
+    if (p.tb != QG_I8 || p.td != QG_I32 || p.qa || p.qb || p.epi) return QG_ERR_UNSUPPORTED;
     if (alpha != 1.f || !(beta == 0.f || beta == 1.f)) return QG_ERR_UNSUPPORTED;
   } else if (float16ish) {
     if (p.tb == QG_U4) {
@@ -198,7 +223,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     } else if (p.tb != p.ta || p.qa || p.qb) {
       return QG_ERR_UNSUPPORTED;
     }
-    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16)) return QG_ERR_UNSUPPORTED;
+    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16 || p.td == QG_I8)) return QG_ERR_UNSUPPORTED;
   } else if (p.ta == QG_E4M3) {
     // block-scaled fp8: U fp32 per row and 128-deep k group, V fp32 per
     // 128 x 128 block of B (per expert when grouped)
@@ -224,10 +249,12 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     p.V = V;
     p.ldu = Ud->ld;
     p.ldv = Vd->ld;
-    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16)) return QG_ERR_UNSUPPORTED;
+    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16 || p.td == QG_I8)) return QG_ERR_UNSUPPORTED;
   } else {
     return QG_ERR_UNSUPPORTED;
   }
+  // int8 output only as quantised codes, and quantised codes only as int8
+  if ((p.td == QG_I8) != ((p.epi & QG_EPI_QUANT_I8) != 0)) return QG_ERR_UNSUPPORTED;
   // pointers, leading dimensions, alignment
   if (p.M > 0 && p.N > 0) {
     if (!D) return QG_ERR_INVALID_ARG;
@@ -325,6 +352,11 @@ int make_plan(const qg_handle* h, const Problem& p, const Choice& c, const qg_wo
   a.d_type = p.td;
   a.zero_point = p.zp;
   a.group_k = p.group_k;
+  a.epi = p.epi;
+  a.bias_type = p.bias_type;
+  a.bias = p.bias;
+  a.row_scale = p.row_scale;
+  a.out_zero_point = p.out_zp;
   a.tiles_n = (int32_t)cdiv(p.N, k.bn);
   a.iters = (int32_t)cdiv(p.K, k.bk);
   a.group_m = 4;
@@ -791,7 +823,7 @@ int qg_export(qg_handle* h, char* buf, size_t cap, size_t* len) {
   std::ostringstream os;
   {
     std::lock_guard<std::mutex> g(h->mu);
-    os << "qgemm-cache 1 arch=" << h->arch << " entries=" << h->cache.size() << "\n";
+    os << "qgemm-cache 2 arch=" << h->arch << " entries=" << h->cache.size() << "\n";
     for (auto& kv : h->cache) {
       const Entry& e = kv.second;
       char line[256];
@@ -818,7 +850,7 @@ int qg_import(qg_handle* h, const char* buf, size_t len) {
     std::istringstream hs(line);
     std::string magic, ver, arch, entries;
     hs >> magic >> ver >> arch >> entries;
-    if (magic != "qgemm-cache" || ver != "1") return QG_ERR_FORMAT;
+    if (magic != "qgemm-cache" || ver != "2") return QG_ERR_FORMAT;  // version 2: keys carry the epilogue flags
     if (arch != "arch=" + h->arch) return QG_ERR_FORMAT;
     if (entries.rfind("entries=", 0) != 0) return QG_ERR_FORMAT;
     long n = strtol(entries.c_str() + 8, nullptr, 10);

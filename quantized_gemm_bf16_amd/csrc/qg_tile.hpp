@@ -137,11 +137,67 @@ __device__ __forceinline__ void store_d4(const Args& a, int64_t m, int n, const 
   }
 }
 
-// D = alpha * acc (+ beta * c, c already loaded) -> D
+// Fused epilogue steps after alpha/beta (the DeepGEMM write-up, section 6:
+// bias and activation, then per-row output quantisation). The flags are
+// kernel arguments: uniform branches, evaluated once per 4 outputs.
+__device__ __forceinline__ void epi_fused(const Args& a, int64_t m, int n, float v[4]) {
+  if (a.epi & EPI_BIAS) {
+    float b[4];
+    const bool full = n + 3 < a.N;
+    if (a.bias_type == DT_F32) {
+      const float* p = (const float*)a.bias + n;
+      if (full) {
+        const f32x4 x = *(const f32x4*)p;
+        b[0] = x[0], b[1] = x[1], b[2] = x[2], b[3] = x[3];
+      } else
+        for (int j = 0; j < 4; ++j) b[j] = (n + j < a.N) ? p[j] : 0.f;
+    } else {
+      const uint16_t* p = (const uint16_t*)a.bias + n;
+      uint16_t h[4];
+      if (full) {
+        const u16x4 x = *(const u16x4*)p;
+        h[0] = x[0], h[1] = x[1], h[2] = x[2], h[3] = x[3];
+      } else
+        for (int j = 0; j < 4; ++j) h[j] = (n + j < a.N) ? p[j] : 0;
+      for (int j = 0; j < 4; ++j) b[j] = a.bias_type == DT_BF16 ? bf16_bits_to_f32(h[j]) : f16_bits_to_f32(h[j]);
+    }
+    for (int j = 0; j < 4; ++j) v[j] += b[j];
+  }
+  if (a.epi & EPI_RELU)
+    for (int j = 0; j < 4; ++j) v[j] = v[j] > 0.f ? v[j] : 0.f;
+  if (a.epi & EPI_GELU)
+    for (int j = 0; j < 4; ++j) v[j] = 0.5f * v[j] * (1.f + erff(v[j] * 0.70710678118654752f));
+}
+
+// int8 output codes: saturate(round_half_even(x * row_scale[m] + zero_point))
+__device__ __forceinline__ void store_q4(const Args& a, int64_t m, int n, const float v[4]) {
+  const float s = a.row_scale[m];
+  int q[4];
+  for (int j = 0; j < 4; ++j) {
+    const float t = rintf(__builtin_fmaf(v[j], s, a.out_zero_point));
+    q[j] = (int)fminf(fmaxf(t, -128.f), 127.f);
+  }
+  int8_t* p = (int8_t*)a.D + m * a.ldd + n;
+  if (n + 3 < a.N)
+    *(uint32_t*)p = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+                    ((uint32_t)(q[3] & 0xFF) << 24);
+  else
+    for (int j = 0; j < 4; ++j)
+      if (n + j < a.N) p[j] = (int8_t)q[j];
+}
+
+// D = alpha * acc (+ beta * c, c already loaded), then the fused steps -> D
 __device__ __forceinline__ void epi_store4c(const Args& a, int64_t m, int n, const f32x4& acc, const f32x4& c) {
   float v[4] = {a.alpha * acc[0], a.alpha * acc[1], a.alpha * acc[2], a.alpha * acc[3]};
   if (a.c_type >= 0 && a.beta != 0.f)
     for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(a.beta, c[j], v[j]);
+  if (a.epi) {
+    epi_fused(a, m, n, v);
+    if (a.epi & EPI_QUANT_I8) {
+      store_q4(a, m, n, v);
+      return;
+    }
+  }
   store_d4(a, m, n, v);
 }
 

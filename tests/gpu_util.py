@@ -7,7 +7,8 @@ import torch
 
 import quantized_gemm_bf16_amd as qg
 
-_TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i32": torch.int32}
+_TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i32": torch.int32,
+              "i8": torch.int8}
 
 
 def dev(arr):
@@ -49,8 +50,8 @@ class Run:
         M, N, K = p["M"], p["N"], p["K"]
         self.A = dev(p["A"])
         self.B = dev(p["B"])
-        # C and D rows are padded to a multiple of 8 elements (16-byte row pitch)
-        self.ldn = -(-N // 8) * 8
+        # C and D rows are padded to a 16-byte row pitch (8 elements; 16 for int8 D)
+        self.ldn = -(-N // 16) * 16 if self.out == "i8" else -(-N // 8) * 8
         self.C = None
         if p.get("C") is not None:
             cp = np.zeros((M, self.ldn), dtype=p["C"].dtype)
@@ -72,8 +73,8 @@ class Run:
             Vp = np.zeros(V.shape[:-1] + (self.ldv,), dtype=V.dtype)
             Vp[..., :V.shape[-1]] = V
             self.V = dev(Vp)
-        self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") if self.out != "i32" \
-            else torch.full((M, self.ldn), -7, dtype=torch.int32, device="cuda")
+        self.D = torch.full((M, self.ldn), float("nan"), dtype=_TORCH_OUT[self.out], device="cuda") \
+            if self.out not in ("i32", "i8") else torch.full((M, self.ldn), -7, dtype=_TORCH_OUT[self.out], device="cuda")
         kind = p["kind"]
         if p.get("batched"):
             # batched: every descriptor gives ONE batch; A/C/D batches back to back
@@ -139,7 +140,7 @@ class Run:
         torch.cuda.synchronize()
         D = host_f64(self.D)
         pad = D[:, self.p["N"]:]
-        if self.out == "i32":
+        if self.out in ("i32", "i8"):
             assert (pad == -7).all(), "write past column N"
         else:
             assert np.isnan(pad).all(), "write past column N"

@@ -153,9 +153,9 @@ def test_tuning_sequence(g):
     assert seq[0] == 1 and seq == sorted(seq) and 16 in seq and 4096 in seq and len(seq) == len(set(seq))
 
 
-CACHE = """qgemm-cache 1 arch=gfx950 entries=2
-16|bf16.bf16.-.bf16.q00.e0.n4096.k14336 kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
-4096|bf16.bf16.-.bf16.q00.e0.n4096.k4096 kernel=tile_BF16_128x128x128b_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
+CACHE = """qgemm-cache 2 arch=gfx950 entries=2
+16|bf16.bf16.-.bf16.q00.e0.x0.n4096.k14336 kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
+4096|bf16.bf16.-.bf16.q00.e0.x0.n4096.k4096 kernel=tile_BF16_128x128x128b_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
 """
 
 
@@ -165,7 +165,7 @@ def test_cache_import_export_roundtrip_and_lookup():
     assert g.import_(CACHE) == qg.OK
     assert g.cache_size() == 2
     out = g.export()
-    assert out.splitlines()[0] == "qgemm-cache 1 arch=gfx950 entries=2"
+    assert out.splitlines()[0] == "qgemm-cache 2 arch=gfx950 entries=2"
     assert sorted(out.splitlines()[1:]) == sorted(CACHE.splitlines()[1:])
     g2 = qg.Gemm()
     assert g2.import_(out) == qg.OK and g2.export() == out
@@ -184,8 +184,8 @@ def test_cache_import_export_roundtrip_and_lookup():
 @pytest.mark.parametrize("bad", [
     "",
     "nonsense\n",
-    "qgemm-cache 2 arch=gfx950 entries=0\n",
-    "qgemm-cache 1 arch=gfx942 entries=0\n",
+    "qgemm-cache 1 arch=gfx950 entries=0\n",
+    "qgemm-cache 2 arch=gfx942 entries=0\n",
     CACHE.replace("entries=2", "entries=3"),
     CACHE.replace("kernel=tile_BF16_32x64x128b_w1x2_s6", "kernel=no_such_kernel"),
     CACHE.replace("schedule=dp", "schedule=zigzag"),
@@ -297,3 +297,52 @@ def test_batched_validation_and_plan(g):
     q = qg.operation(quant_b=(qg.QUANT_INT4_ZP, 128, 1, 8))
     assert run(g, op=q, Ad=Ad, Bd=qg.layout("u4", N, K, num=E, stride=N * K // 8), Dd=Dd, V=FAKE,
                Vd=qg.layout("f16", N, K // 128, num=E, stride=N * K // 128)) == qg.ERR_UNSUPPORTED
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # compile a probe against include/qgemm.h and compare sizes and offsets with the ctypes mirrors
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "qgemm.h"
+int main(void) {
+  printf("layout %zu %zu %zu %zu\\n", sizeof(qg_layout), offsetof(qg_layout, num), offsetof(qg_layout, offsets),
+         offsetof(qg_layout, stride));
+  printf("quant %zu\\n", sizeof(qg_quant));
+  printf("epi %zu %zu %zu\\n", sizeof(qg_epilogue_args), offsetof(qg_epilogue_args, row_scale),
+         offsetof(qg_epilogue_args, zero_point));
+  printf("op %zu %zu %zu %zu\\n", sizeof(qg_operation), offsetof(qg_operation, schedule),
+         offsetof(qg_operation, kernel), offsetof(qg_operation, epi));
+  printf("ws %zu %zu\\n", sizeof(qg_workspace), offsetof(qg_workspace, partials));
+  return 0;
+}
+""")
+    import subprocess
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict((l.split()[0], [int(x) for x in l.split()[1:]]) for l in subprocess.check_output([str(exe)]).decode().splitlines())
+    C = ctypes
+    assert got["layout"] == [C.sizeof(qg.Layout), qg.Layout.num.offset, qg.Layout.offsets.offset, qg.Layout.stride.offset]
+    assert got["quant"] == [C.sizeof(qg.Quant)]
+    assert got["epi"] == [C.sizeof(qg.EpilogueArgs), qg.EpilogueArgs.row_scale.offset, qg.EpilogueArgs.zero_point.offset]
+    assert got["op"] == [C.sizeof(qg.Operation), qg.Operation.schedule.offset, qg.Operation.kernel.offset,
+                         qg.Operation.epi.offset]
+    assert got["ws"] == [C.sizeof(qg.Workspace), qg.Workspace.partials.offset]
+
+
+def test_epilogue_validation(g):
+    Ad, Bd, Dd = dense(64, 64, 64)
+    E = qg
+    assert run(g, op=qg.operation(epilogue=E.EPI_RELU | E.EPI_GELU), Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, op=qg.operation(epilogue=E.EPI_BIAS), Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, op=qg.operation(epilogue=E.EPI_BIAS, bias=FAKE + 4), Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_ALIGNMENT
+    assert run(g, op=qg.operation(epilogue=E.EPI_BIAS, bias=FAKE, bias_type="i32"), Ad=Ad, Bd=Bd, Dd=Dd) == \
+        qg.ERR_UNSUPPORTED
+    q = qg.operation(epilogue=E.EPI_QUANT_I8, row_scale=FAKE)
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_UNSUPPORTED                 # D must be int8
+    assert run(g, Ad=Ad, Bd=Bd, Dd=qg.layout("i8", 64, 64)) == qg.ERR_UNSUPPORTED  # int8 D needs QUANT_I8
+    d = g.plan(q, Ad, None, Bd, None, None, qg.layout("i8", 64, 64), 1.0, 0.0, ws_desc())
+    assert d.startswith("kernel=")
+    i8 = dense(64, 64, 64, "i8", "i32")
+    assert run(g, op=qg.operation(epilogue=E.EPI_RELU), Ad=i8[0], Bd=i8[1], Dd=i8[2]) == qg.ERR_UNSUPPORTED

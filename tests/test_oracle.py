@@ -403,3 +403,54 @@ def test_batched_problem_matches_numpy_per_batch():
         want = 0.5 * (a[rows] @ b.T) + 2.0 * c[rows]
         assert np.allclose(ref[rows], want, rtol=1e-12, atol=1e-12)
     assert np.array_equal(p["B"][1], p["B"][0]) and np.array_equal(p["B"][2], p["B"][0])
+
+
+# ---------------------------------------------------------------- fused epilogue
+def _epi_problem(flags, bias=None, bias_type="f32", row_scale=None, zero_point=0.0, seed=31, M=6, N=40, K=32):
+    p = synth.dense_problem(M, N, K, "bf16", "f32", c_dtype="f32", alpha=0.75, beta=0.5, dist="uniform", seed=seed)
+    p["epilogue"] = dict(flags=flags, bias=bias, bias_type=bias_type, row_scale=row_scale, zero_point=zero_point)
+    return p
+
+
+def test_epilogue_bias_adds_per_column():
+    bias = synth.uniform((40,), -2, 2, 5).astype(np.float32)
+    p = _epi_problem(1, bias=bias)
+    q = dict(p, epilogue=None)
+    ref, _ = oracle.gemm(p)
+    ref0, _ = oracle.gemm(q)
+    assert np.array_equal(ref, ref0 + bias.astype(np.float64)[None, :])
+    # a bf16 bias decodes like any bf16 operand
+    bb = synth.to_bf16_bits(bias)
+    refb, _ = oracle.gemm(_epi_problem(1, bias=bb, bias_type="bf16"))
+    assert np.array_equal(refb, ref0 + _bf16_to_f64(bb)[None, :])
+
+
+def test_epilogue_relu_and_gelu():
+    bias = synth.uniform((40,), -2, 2, 6).astype(np.float32)
+    x, _ = oracle.gemm(_epi_problem(1, bias=bias))
+    relu, _ = oracle.gemm(_epi_problem(1 | 2, bias=bias))
+    assert np.array_equal(relu, np.maximum(x, 0.0))
+    gelu, _ = oracle.gemm(_epi_problem(1 | 4, bias=bias))
+    from scipy.special import erf
+    assert np.allclose(gelu, 0.5 * x * (1 + erf(x / np.sqrt(2))), rtol=1e-14, atol=1e-15)
+    # closed forms: gelu(x) - gelu(-x) = x; gelu(0) = 0; gelu(x) -> x for large x, -> 0 for very negative x
+    neg = _epi_problem(1 | 4, bias=-bias)
+    neg["alpha"], neg["beta"] = -0.75, -0.5
+    gneg, _ = oracle.gemm(neg)
+    assert np.allclose(gelu - gneg, x, rtol=0, atol=1e-13)
+
+
+def test_quantisation_rounding_and_saturation():
+    # ref values chosen directly: ties go to even, values past the int8 range saturate
+    M, N = 2, 8
+    p = _epi_problem(8, row_scale=np.array([1.0, 0.5], dtype=np.float32), zero_point=0.0, M=M, N=N)
+    ref = np.array([[0.5, 1.5, 2.5, -0.5, -1.5, 200.0, -300.0, 126.6],
+                    [5.0, 3.0, -5.0, 1.0, 253.0, 256.0, -257.0, -258.0]])
+    pre, code = oracle.quant_codes(p, ref)
+    assert np.array_equal(code[0], [0, 2, 2, 0, -2, 127, -128, 127])
+    assert np.array_equal(code[1], [2, 2, -2, 0, 126, 127, -128, -128])
+    assert np.array_equal(pre[1], ref[1] * 0.5)
+    # the zero point is added before rounding
+    p["epilogue"]["zero_point"] = 3.0
+    _, code3 = oracle.quant_codes(p, ref)
+    assert np.array_equal(code3[0], [4, 4, 6, 2, 2, 127, -128, 127])
