@@ -211,6 +211,11 @@ size_t qg_partials_size(void);
  *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128)
  *   A, B e4m3 + U, V fp32 (QG_QUANT_BLOCK_F32 on both; A 1 x 128, B 128 x 128)
  *   A, B int8 -> D int32, C int32; alpha must be 1 and beta 0 or 1 (exact)
+ *   A, B int8 + U, V fp32 (w8a8: QG_QUANT_BLOCK_F32 on both with group_mn = 1
+ *     and group_k = 0 or >= K, i.e. one scale per row of A and per row of B;
+ *     U is M x >=1, V is N x >=1, any ld >= 1, 4-byte aligned) -> the exact
+ *     int32 sum times U[m] * V[n] in fp32, then the float epilogue; D f32 |
+ *     bf16 | fp16 (or int8 codes), C f32 | bf16 | fp16; not grouped/batched
  *   float paths with QG_EPI_QUANT_I8 -> D int8
  *   any of these grouped over experts (Adesc.num = Bdesc.num = E, offsets),
  *   and all but int4 batched (num = batch count on every operand, no offsets).

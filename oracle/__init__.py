@@ -163,6 +163,12 @@ def _problem(p: dict, splits: int, alpha, beta, keep):
             st.qa = st.qb = Q_BLOCK
             st.U, st.ldu, st.gm_a, st.gk_a = _ptr(U), U.shape[1], 1, p["group_k"]
             st.V, st.ldv, st.gn_b, st.gk_b = _ptr(V), V.shape[1], p["group_n"], p["group_k"]
+        elif p.get("w8a8"):
+            # one scale per row of A and per row of B: 1 x K blocks
+            U, V = c(p["U"]), c(p["V"])
+            st.qa = st.qb = Q_BLOCK
+            st.U, st.ldu, st.gm_a, st.gk_a = _ptr(U), U.shape[1], 1, max(K, 1)
+            st.V, st.ldv, st.gn_b, st.gk_b = _ptr(V), V.shape[1], 1, max(K, 1)
     ep = p.get("epilogue")
     if ep:
         st.epi = int(ep["flags"])

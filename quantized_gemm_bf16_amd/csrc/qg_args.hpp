@@ -31,6 +31,7 @@ struct Args {
 
   // epilogue (flags as in the C ABI's qg_epilogue)
   int32_t epi;
+  int32_t int_scaled;                    // int8 sums scaled by U[m*ldu] * V[n*ldv] (w8a8)
   int32_t bias_type;
   const void* bias;                      // N values, or null
   const float* row_scale;                // output quantisation: one per row of D

@@ -86,6 +86,7 @@ struct Problem {
   const void* bias = nullptr;
   const float* row_scale = nullptr;
   float out_zp = 0.f;
+  bool w8a8 = false;  // int8 A, B with fp32 scales per row of A and per row of B
 
   std::string key() const {
     char buf[160];
@@ -202,8 +203,30 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   }
   // dtype combinations
   const bool float16ish = (p.ta == QG_BF16 || p.ta == QG_F16);
-  if (p.ta == QG_I8) {
-    if (p.tb != QG_I8 || p.td != QG_I32 || p.qa || p.qb || p.epi) return QG_ERR_UNSUPPORTED;
+  if (p.ta == QG_I8 && (p.qa || p.qb)) {
+    // w8a8: a(i,k) = qa * U[i], b(j,k) = qb * V[j] (fp32 scales over whole
+    // rows: block quantisation with group_mn = 1 and group_k covering K);
+    // exact int32 sums, then the float epilogue
+    if (p.tb != QG_I8 || p.qa != QG_QUANT_BLOCK_F32 || p.qb != QG_QUANT_BLOCK_F32) return QG_ERR_UNSUPPORTED;
+    const qg_quant &qa = op->quant_a, &qb = op->quant_b;
+    if (qa.group_mn != 1 || qb.group_mn != 1) return QG_ERR_UNSUPPORTED;
+    if ((qa.group_k != 0 && qa.group_k < p.K) || (qb.group_k != 0 && qb.group_k < p.K)) return QG_ERR_UNSUPPORTED;
+    if (grouped) return QG_ERR_UNSUPPORTED;
+    if (!Ud || !Vd) return QG_ERR_INVALID_ARG;
+    if ((st = check_layout(Ud)) || (st = check_layout(Vd))) return st;
+    if (Ud->type != QG_F32 || Vd->type != QG_F32) return QG_ERR_UNSUPPORTED;
+    if (Ud->rows != p.M || Vd->rows != p.N || Ud->cols < 1 || Vd->cols < 1 || Ud->ld < 1 || Vd->ld < 1)
+      return QG_ERR_INVALID_ARG;
+    if (p.M > 0 && p.N > 0 && (!U || !V)) return QG_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(U) & 3) || (reinterpret_cast<uintptr_t>(V) & 3)) return QG_ERR_ALIGNMENT;
+    if (!(p.td == QG_F32 || p.td == QG_BF16 || p.td == QG_F16 || p.td == QG_I8)) return QG_ERR_UNSUPPORTED;
+    p.w8a8 = true;
+    p.U = U;
+    p.V = V;
+    p.ldu = Ud->ld;
+    p.ldv = Vd->ld;
+  } else if (p.ta == QG_I8) {
+    if (p.tb != QG_I8 || p.td != QG_I32 || p.epi) return QG_ERR_UNSUPPORTED;
     if (alpha != 1.f || !(beta == 0.f || beta == 1.f)) return QG_ERR_UNSUPPORTED;
   } else if (float16ish) {
     if (p.tb == QG_U4) {
@@ -282,7 +305,7 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
     if (!C || !Cd) return QG_ERR_INVALID_ARG;
     if ((st = check_layout(Cd))) return st;
     if (Cd->rows != p.M || Cd->cols != p.N || Cd->ld < p.N) return QG_ERR_INVALID_ARG;
-    if (p.ta == QG_I8) {
+    if (p.ta == QG_I8 && !p.w8a8) {
       if (Cd->type != QG_I32) return QG_ERR_UNSUPPORTED;
     } else if (!(Cd->type == QG_F32 || Cd->type == QG_BF16 || Cd->type == QG_F16)) {
       return QG_ERR_UNSUPPORTED;
@@ -353,6 +376,7 @@ int make_plan(const qg_handle* h, const Problem& p, const Choice& c, const qg_wo
   a.zero_point = p.zp;
   a.group_k = p.group_k;
   a.epi = p.epi;
+  a.int_scaled = p.w8a8 ? 1 : 0;
   a.bias_type = p.bias_type;
   a.bias = p.bias;
   a.row_scale = p.row_scale;

@@ -207,8 +207,20 @@ __device__ __forceinline__ void epi_store4(const Args& a, int64_t m, int n, cons
   epi_store4c(a, m, n, acc, f32x4{c[0], c[1], c[2], c[3]});
 }
 
-// int8 path: D = acc (+ C when beta == 1), exact int32.
+// int8 path: D = acc (+ C when beta == 1), exact int32; with per-row scales
+// of A and B (w8a8) the exact sum is scaled in fp32 and takes the float
+// epilogue: x = acc * U[m] * V[n].
 __device__ __forceinline__ void epi_store4(const Args& a, int64_t m, int n, const i32x4& acc) {
+  if (a.int_scaled) {
+    const float sa = ((const float*)a.U)[m * a.ldu];
+    const float* vb = (const float*)a.V;
+    f32x4 x;
+    for (int j = 0; j < 4; ++j) x[j] = (n + j < a.N) ? (float)acc[j] * sa * vb[(int64_t)(n + j) * a.ldv] : 0.f;
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.c_type >= 0 && a.beta != 0.f) load_c4(a, m, n, c);
+    epi_store4c(a, m, n, x, f32x4{c[0], c[1], c[2], c[3]});
+    return;
+  }
   int v[4] = {acc[0], acc[1], acc[2], acc[3]};
   const bool full = n + 3 < a.N;
   if (a.c_type == DT_I32 && a.beta != 0.f) {

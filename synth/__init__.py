@@ -195,6 +195,18 @@ def dense_fp8_problem(M, N, K, out_dtype=BF16, c_dtype=None, alpha=1.0, beta=0.0
     return p
 
 
+def w8a8_problem(M, N, K, out_dtype=BF16, c_dtype=None, alpha=1.0, beta=0.0, seed=SEED_A, s_lo=0.001, s_hi=0.01):
+    """int8 A [M,K], B [N,K] uniform over [-128, 127] with fp32 scales per row of
+    A (U [M, 1]) and per row of B (V [N, 1]) ~ U[s_lo, s_hi]; C ~ N(0, 1)."""
+    p = dict(kind="dense", M=M, N=N, K=K, in_dtype=I8, out_dtype=out_dtype, c_dtype=c_dtype,
+             alpha=float(alpha), beta=float(beta), w8a8=True,
+             A=int8_uniform((M, K), seed), B=int8_uniform((N, K), seed + 1),
+             U=uniform((M, 1), s_lo, s_hi, seed + 3), V=uniform((N, 1), s_lo, s_hi, seed + 4))
+    if c_dtype is not None:
+        p["C"] = to_storage(normal((M, N), 1.0, seed + 2), c_dtype)
+    return p
+
+
 def w4a16_problem(M, N, K, group=128, seed=SEED_A, out_dtype=BF16, a_std=1.0,
                   s_lo=0.005, s_hi=0.02, zero_point=8):
     """A bf16 [M,K] ~ N(0,a_std); B int4 nibbles uniform 0..15 packed [N, K/8];

@@ -113,6 +113,11 @@ class Run:
             nb, kg = p["V"].shape[1], p["V"].shape[2]
             self.Ud = qg.layout("f32", M, p["U"].shape[1], ld=self.ldu, num=p["E"], offsets=self.off.data_ptr())
             self.Vd = qg.layout("f32", nb, kg, ld=self.ldv, num=p["E"], stride=nb * self.ldv)
+        elif p.get("w8a8"):
+            # per-row scale vectors, unpadded (ld 1)
+            self.U, self.V = dev(p["U"]), dev(p["V"])
+            self.Ud = qg.layout("f32", M, 1, ld=1)
+            self.Vd = qg.layout("f32", N, 1, ld=1)
         elif p.get("U") is not None:
             self.Ud = qg.layout("f32", M, p["U"].shape[1], ld=self.ldu)
             self.Vd = qg.layout("f32", p["V"].shape[0], p["V"].shape[1], ld=self.ldv)
@@ -120,6 +125,9 @@ class Run:
     def op(self, **kw):
         if self.p["kind"] == "w4a16":
             kw.setdefault("quant_b", (qg.QUANT_INT4_ZP, self.p["group"], 1, self.p["zero_point"]))
+        if self.p.get("w8a8"):
+            kw.setdefault("quant_a", (qg.QUANT_BLOCK_F32, 0, 1, 0))
+            kw.setdefault("quant_b", (qg.QUANT_BLOCK_F32, 0, 1, 0))
         if self.p["in_dtype"] == "e4m3":
             kw.setdefault("quant_a", (qg.QUANT_BLOCK_F32, self.p["group_k"], 1, 0))
             kw.setdefault("quant_b", (qg.QUANT_BLOCK_F32, self.p["group_k"], self.p["group_n"], 0))

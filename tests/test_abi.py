@@ -346,3 +346,25 @@ def test_epilogue_validation(g):
     assert d.startswith("kernel=")
     i8 = dense(64, 64, 64, "i8", "i32")
     assert run(g, op=qg.operation(epilogue=E.EPI_RELU), Ad=i8[0], Bd=i8[1], Dd=i8[2]) == qg.ERR_UNSUPPORTED
+
+
+def test_w8a8_validation(g):
+    M, N, K = 64, 128, 256
+    Ad, Bd = qg.layout("i8", M, K), qg.layout("i8", N, K)
+    Dd = qg.layout("bf16", M, N)
+    Ud, Vd = qg.layout("f32", M, 1, ld=1), qg.layout("f32", N, 1, ld=1)
+    q = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 0, 1, 0), quant_b=(qg.QUANT_BLOCK_F32, 0, 1, 0))
+    ok = dict(Ad=Ad, Bd=Bd, Dd=Dd, U=FAKE, Ud=Ud, V=FAKE, Vd=Vd)
+    d = dict(kv.split("=") for kv in g.plan(q, Ad, Ud, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).split())
+    assert d["kernel"].startswith(("tile_I8_", "skinny_I8_"))
+    # scales shorter than a whole row of K, or per block of rows, are not this path
+    q_bad = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 128, 1, 0), quant_b=(qg.QUANT_BLOCK_F32, 0, 1, 0))
+    assert run(g, op=q_bad, **ok) == qg.ERR_UNSUPPORTED
+    q_bad = qg.operation(quant_a=(qg.QUANT_BLOCK_F32, 0, 4, 0), quant_b=(qg.QUANT_BLOCK_F32, 0, 1, 0))
+    assert run(g, op=q_bad, **ok) == qg.ERR_UNSUPPORTED
+    # missing / misshaped / misaligned scales
+    assert run(g, op=q, Ad=Ad, Bd=Bd, Dd=Dd) == qg.ERR_INVALID_ARG
+    assert run(g, op=q, **{**ok, "Ud": qg.layout("f32", M - 1, 1, ld=1)}) == qg.ERR_INVALID_ARG
+    assert run(g, op=q, **{**ok, "V": FAKE + 2}) == qg.ERR_ALIGNMENT
+    # an int32 D belongs to the exact path, not to scaled sums
+    assert run(g, op=q, **{**ok, "Dd": qg.layout("i32", M, N)}) == qg.ERR_UNSUPPORTED

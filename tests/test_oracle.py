@@ -454,3 +454,15 @@ def test_quantisation_rounding_and_saturation():
     p["epilogue"]["zero_point"] = 3.0
     _, code3 = oracle.quant_codes(p, ref)
     assert np.array_equal(code3[0], [4, 4, 6, 2, 2, 127, -128, 127])
+
+
+def test_w8a8_matches_int_sums_times_scales():
+    p = synth.w8a8_problem(9, 33, 80, out_dtype="f32", c_dtype="f32", alpha=2.0, beta=0.5, seed=17)
+    ref, absdot = oracle.gemm(p)
+    s = p["A"].astype(np.int64) @ p["B"].astype(np.int64).T  # exact integer sums
+    u = p["U"][:, 0].astype(np.float64)
+    v = p["V"][:, 0].astype(np.float64)
+    want = 2.0 * s * u[:, None] * v[None, :] + 0.5 * p["C"].astype(np.float64)
+    assert np.allclose(ref, want, rtol=1e-13, atol=1e-13)
+    assert np.allclose(absdot, (np.abs(p["A"].astype(np.int64)) @ np.abs(p["B"].astype(np.int64)).T)
+                       * u[:, None] * v[None, :], rtol=1e-13)
