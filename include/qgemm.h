@@ -79,6 +79,7 @@ typedef enum qg_order { QG_ROW_MAJOR = 0, QG_COL_MAJOR = 1 } qg_order;
  *   type, order  element type and storage order (only QG_ROW_MAJOR today).
  *   rows, cols   logical shape. A: M x K, B: N x K, C/D: M x N,
  *                U (fp8 A scales): ceil(M/group_mn) x ceil(K/group_k) fp32,
+ *                U (int4 zero points): N x K/group_k int8 (values 0..15),
  *                V (int4 scales): N x ceil(K/group_k) fp16,
  *                V (fp8 B scales): ceil(N/group_mn) x ceil(K/group_k) fp32.
  *                For a grouped problem rows of A/C/D/U is the total row count
@@ -150,7 +151,9 @@ typedef struct qg_epilogue_args {
 
 typedef enum qg_quant_kind {
   QG_QUANT_NONE = 0,
-  QG_QUANT_INT4_ZP = 1,   /* B only: b = (q - zero_point) * V[n, k / group_k], V fp16 */
+  QG_QUANT_INT4_ZP = 1,   /* B only: b = (q - zero_point) * V[n, k / group_k], V fp16;
+                             with U given (asymmetric), zero_point = U[n, k / group_k],
+                             U QG_I8 bytes (N x K/group_k, ld a multiple of 16) */
   QG_QUANT_BLOCK_F32 = 2  /* e4m3 A or B: value = code * scale of its (group_mn x group_k) block */
 } qg_quant_kind;
 
@@ -208,7 +211,8 @@ size_t qg_partials_size(void);
  * unused (C only when beta == 0: then C is never read, so NaNs in it do not
  * propagate). alpha == 0 still reads A and B. Supported combinations:
  *   A, B bf16 | fp16            -> D f32 | bf16 | fp16, C f32 | bf16 | fp16
- *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128)
+ *   A bf16, B u4 + V fp16 (QG_QUANT_INT4_ZP on B, group_k = 128), optional
+ *     per-group zero points in U
  *   A, B e4m3 + U, V fp32 (QG_QUANT_BLOCK_F32 on both; A 1 x 128, B 128 x 128)
  *   A, B int8 -> D int32, C int32; alpha must be 1 and beta 0 or 1 (exact)
  *   A, B int8 + U, V fp32 (w8a8: QG_QUANT_BLOCK_F32 on both with group_mn = 1

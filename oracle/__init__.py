@@ -142,6 +142,9 @@ def _problem(p: dict, splits: int, alpha, beta, keep):
         st.B, st.ldb = _ptr(B), K // 8
         st.V, st.ldv = _ptr(V), V.shape[1]
         st.gk_b, st.zero_point = p["group"], p["zero_point"]
+        if p.get("Z") is not None:  # per-group zero points
+            Z = c(np.asarray(p["Z"], dtype=np.int8))
+            st.U, st.ldu = _ptr(Z), Z.shape[1]
     elif kind == "grouped":
         B = c(p["B"])
         off = c(np.asarray(p["offsets"], dtype=np.int32))

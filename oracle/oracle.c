@@ -28,7 +28,8 @@
  *   int8               : the integer
  *   int4 (weight only) : b(j,k) = (q(j,k) - zero_point) * s(j, k / group_k),
  *                        s an fp16 scale, q the nibble k%8 of word k/8 of row j
- *                        (bits [4*(k%8), 4*(k%8)+4))
+ *                        (bits [4*(k%8), 4*(k%8)+4)); asymmetric: zero_point
+ *                        = U(j, k / group_k), one byte per column and group
  *   fp8 OCP E4M3       : a(i,k) = dec(qa) * U(i / group_m, k / group_k),
  *                        b(j,k) = dec(qb) * V(e, j / group_n, k / group_k)
  * Grouped (MoE) problems: row r of A and D belongs to the expert e with
@@ -143,7 +144,9 @@ static double b_value(const or_problem* p, int64_t e, int64_t j, int64_t k) {
     uint32_t word = w[j * p->ldb + k / 8];
     int q = (int)((word >> (4 * (k % 8))) & 15u);
     const uint16_t* s = (const uint16_t*)p->V + e * p->v_batch;
-    return (double)(q - p->zero_point) * or_dec_f16(s[j * p->ldv + k / p->gk_b]);
+    /* asymmetric: a zero point per column and group, bytes in U */
+    int zp = p->U ? (int)((const int8_t*)p->U)[j * p->ldu + k / p->gk_b] : p->zero_point;
+    return (double)(q - zp) * or_dec_f16(s[j * p->ldv + k / p->gk_b]);
   }
   int64_t esz = (p->tb == OR_F32) ? 4 : (p->tb == OR_F16 || p->tb == OR_BF16) ? 2 : 1;
   const char* base = (const char*)p->B + e * p->b_batch * esz;

@@ -243,6 +243,17 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
       p.ldv = Vd->ld;
       p.zp = op->quant_b.zero_point;
       p.group_k = 128;
+      // optional per-group zero points (asymmetric int4): one byte per column
+      // and group in U, replacing the constant zero point
+      if (U || Ud) {
+        if (!U || !Ud) return QG_ERR_INVALID_ARG;
+        if ((st = check_layout(Ud))) return st;
+        if (Ud->type != QG_I8) return QG_ERR_UNSUPPORTED;
+        if (Ud->rows != p.N || Ud->cols != p.K / 128 || Ud->ld < Ud->cols) return QG_ERR_INVALID_ARG;
+        if (Ud->ld % 16 || !aligned16(U)) return QG_ERR_ALIGNMENT;
+        p.U = U;
+        p.ldu = Ud->ld;
+      }
     } else if (p.tb != p.ta || p.qa || p.qb) {
       return QG_ERR_UNSUPPORTED;
     }

@@ -2,6 +2,8 @@
 // uint32 (element k = 8w + i in bits [4i, 4i+4) of word w), fp16 scale per
 // (column n, 128-deep group of k), zero point zp:
 //     b(n, k) = (q(n, k) - zp) * s(n, k / 128)
+// where zp is one constant, or (asymmetric) a zero point per column and group
+// held as a byte in U: zp = U[n, k / 128]
 // (the "U, V quantization scale operands" of the page "InternLM Lmdeploy Gemm
 // Interface", I/O Contract, and the group tracking of the page "InternLM
 // Lmdeploy Gemm MainloopSm80V2": the scale advances once per group along K).
@@ -36,10 +38,11 @@ struct W4Cfg {
   // scales: every lane of a dword load writes LDS, so each wave gets 64 dword
   // slots; lanes past its BN/NW columns load nothing (zeros).
   static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB, S_BYTES = NW * 64 * 4;
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int Z_BYTES = NW * 64 * 4;  // per-group zero points (a dword per lane)
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + Z_BYTES;
   static constexpr int LA = BM / 4 / NW;   // 64-lane A loads per wave (4 rows x 256 B each)
   static constexpr int LB = BN / 16 / NW;  // 64-lane B loads per wave (16 rows x 64 B each)
-  static constexpr int LPW = LA + LB + 1;  // + one scale load (BN/NW rows, dword each)
+  static constexpr int LPW = LA + LB + 2;  // + one scale load and one zero-point load (dword each)
   static_assert(LA * 4 * NW == BM && LB * 16 * NW == BN, "rows must split over waves");
   static_assert(BNW % 16 == 0 && BNW <= 64, "columns per wave");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024 - 4096, "LDS budget");
@@ -63,6 +66,11 @@ struct W4 {
     const i32x4 rA = make_rsrc_words((const char*)a.A + (int64_t)u.m0 * lda_b, (uint32_t)(a_rows * lda_b));
     const i32x4 rB = make_rsrc_words((const char*)a.B + (int64_t)u.n0 * ldb_b, (uint32_t)(b_rows * ldb_b));
     const i32x4 rV = make_rsrc_words((const char*)a.V + (int64_t)u.n0 * ldv_b, (uint32_t)(b_rows * ldv_b));
+    // per-group zero points (bytes, U[n, group]); without them the loads read nothing
+    const bool has_z = a.U != nullptr;
+    const int64_t ldz_b = a.ldu;
+    const i32x4 rZ = make_rsrc_words(has_z ? (const char*)a.U + (int64_t)u.n0 * ldz_b : (const char*)a.V,
+                                     has_z ? (uint32_t)(b_rows * ldz_b) : 0u);
 
     // load addressing (lane -> LDS position fixed; the lane fetches the
     // logical chunk the swizzle stores there)
@@ -96,6 +104,9 @@ struct W4 {
       // dword (aligned) that holds s(n0 + srow, kt); ldv is even, so the half is kt & 1
       const uint32_t soff = (uint32_t)(srow * ldv_b) + ((uint32_t)kt * 2 & ~3u);
       load_lds_x1a(rV, sb + Cfg::A_BYTES + Cfg::B_BYTES + w * 256, live && s_lane ? soff : kOOB);
+      // dword (aligned) that holds z(n0 + srow, kt): byte kt & 3 of it (ldu is a multiple of 4)
+      const uint32_t zo = (uint32_t)(srow * ldz_b) + ((uint32_t)kt & ~3u);
+      load_lds_x1a(rZ, sb + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::S_BYTES + w * 256, live && s_lane && has_z ? zo : kOOB);
     };
 
     const int orow = l & 15, og = l >> 4;
@@ -150,19 +161,21 @@ struct W4 {
       }
       // acc += s_n * (P - (128 + zp) * R); lane holds columns n = 4*og + r of each n-tile
       const int half = kt & 1;
+      const uint32_t* sZ = (const uint32_t*)((const char*)sS + Cfg::S_BYTES);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        float s[4];
+        float s[4], zo[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint32_t dw = sS[w * 64 + tn * 16 + 4 * og + r];
           s[r] = f16_bits_to_f32((uint16_t)(half ? dw >> 16 : dw & 0xFFFF));
+          zo[r] = has_z ? 128.0f + (float)((sZ[w * 64 + tn * 16 + 4 * og + r] >> (8 * (kt & 3))) & 0xFFu) : zoff;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc.v[tn][mt][r] = __builtin_fmaf(s[r], __builtin_fmaf(-zoff, R[mt][r], P[tn][mt][r]), acc.v[tn][mt][r]);
+            acc.v[tn][mt][r] = __builtin_fmaf(s[r], __builtin_fmaf(-zo[r], R[mt][r], P[tn][mt][r]), acc.v[tn][mt][r]);
       }
     };
 

@@ -102,6 +102,13 @@ class Run:
         self.Ud = self.Vd = None
         if kind == "w4a16":
             self.Vd = qg.layout("f16", N, p["V"].shape[1], ld=self.ldv)
+            if p.get("Z") is not None:  # per-group zero points, rows padded to 16 bytes
+                Z = p["Z"]
+                ldz = -(-Z.shape[1] // 16) * 16
+                Zp = np.zeros((Z.shape[0], ldz), dtype=np.int8)
+                Zp[:, :Z.shape[1]] = Z
+                self.U = dev(Zp)
+                self.Ud = qg.layout("i8", N, Z.shape[1], ld=ldz)
         if p.get("U") is not None and p.get("batched"):
             nb, kg = p["V"].shape[1], p["V"].shape[2]
             Mb = p["batch_M"]

@@ -368,3 +368,17 @@ def test_w8a8_validation(g):
     assert run(g, op=q, **{**ok, "V": FAKE + 2}) == qg.ERR_ALIGNMENT
     # an int32 D belongs to the exact path, not to scaled sums
     assert run(g, op=q, **{**ok, "Dd": qg.layout("i32", M, N)}) == qg.ERR_UNSUPPORTED
+
+
+def test_w4a16_asymmetric_zero_point_validation(g):
+    M, N, K = 64, 512, 1024
+    Ad, Bd, Dd = qg.layout("bf16", M, K), qg.layout("u4", N, K), qg.layout("bf16", M, N)
+    Vd = qg.layout("f16", N, K // 128)
+    q = qg.operation(quant_b=(qg.QUANT_INT4_ZP, 128, 1, 8))
+    base = dict(op=q, Ad=Ad, Bd=Bd, Dd=Dd, V=FAKE, Vd=Vd)
+    Ud = qg.layout("i8", N, K // 128, ld=16)
+    assert g.plan(q, Ad, Ud, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).startswith("kernel=w4_")
+    assert run(g, **base, U=FAKE) == qg.ERR_INVALID_ARG                            # U without its layout
+    assert run(g, **base, U=FAKE, Ud=qg.layout("f16", N, K // 128, ld=16)) == qg.ERR_UNSUPPORTED
+    assert run(g, **base, U=FAKE, Ud=qg.layout("i8", N, K // 128 + 1, ld=16)) == qg.ERR_INVALID_ARG
+    assert run(g, **base, U=FAKE, Ud=qg.layout("i8", N, K // 128, ld=8)) == qg.ERR_ALIGNMENT

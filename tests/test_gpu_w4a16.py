@@ -61,3 +61,22 @@ def test_zero_points_and_beta(g, ws, zp):
     p["c_dtype"], p["beta"], p["alpha"] = "bf16", 0.5, 2.0
     p["out_dtype"] = "f32"
     check_against_oracle(p, Run(g, p, ws).run(), what=f"W4A16 zp={zp}")
+
+
+@pytest.mark.parametrize("kname", ["w4_BF16_64x256_w8_s4", "w4_BF16_32x256_w8_s4"])
+@pytest.mark.parametrize("sched", ["dp", "split3"])
+def test_asymmetric_per_group_zero_points(g, ws, kname, sched):
+    p = synth.w4a16_problem(40, 520, 1024, seed=31, asym=True)
+    r = Run(g, p, ws)
+    if sched == "dp":
+        op = r.op(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+    else:
+        op = r.op(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=3, kernel=kidx(kname))
+    print(kname, sched, r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"asym int4 {kname} {sched}")
+
+
+def test_asymmetric_full_size_sampled(g, ws):
+    p = synth.w4a16_problem(64, 8192, 8192, asym=True)
+    r = Run(g, p, ws)
+    check_against_oracle(p, r.run(), rows=sample_rows(64, 12), what="asym W4A16 64x8192x8192")

@@ -466,3 +466,21 @@ def test_w8a8_matches_int_sums_times_scales():
     assert np.allclose(ref, want, rtol=1e-13, atol=1e-13)
     assert np.allclose(absdot, (np.abs(p["A"].astype(np.int64)) @ np.abs(p["B"].astype(np.int64)).T)
                        * u[:, None] * v[None, :], rtol=1e-13)
+
+
+def test_int4_asymmetric_zero_points():
+    # per-group zero points: numpy dequant with Z in place of the constant
+    p = synth.w4a16_problem(3, 16, 256, seed=23, asym=True)
+    ref, _ = oracle.gemm(p)
+    N, K = 16, 256
+    words = p["B"].astype(np.uint64)
+    q = np.stack([(words >> np.uint64(4 * i)) & np.uint64(15) for i in range(8)], axis=2).reshape(N, K).astype(np.int64)
+    z = np.repeat(p["Z"].astype(np.int64), 128, axis=1)
+    s = np.repeat(p["V"].view(np.float16).astype(np.float64), 128, axis=1)
+    want = _bf16_to_f64(p["A"]) @ ((q - z) * s).T
+    assert np.allclose(ref, want, rtol=1e-12, atol=1e-12)
+    # a zero point equal to every nibble of its group zeroes that group's contribution
+    p2 = dict(p, Z=np.zeros_like(p["Z"]))
+    p2["B"] = synth.pack_int4(np.zeros((N, K), dtype=np.int64))
+    ref2, _ = oracle.gemm(p2)
+    assert np.array_equal(ref2, np.zeros_like(ref2))
