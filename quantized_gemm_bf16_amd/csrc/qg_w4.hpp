@@ -25,6 +25,8 @@
 // 16g..16g+15) takes k 32g + 8j + {0,4,1,5,2,6,3,7}; A fragments are
 // byte-permuted into that order (v_perm), B comes out of the AND/OR in it.
 #pragma once
+#include <type_traits>
+
 #include "qg_skinny.hpp"
 
 namespace qg {
@@ -162,21 +164,31 @@ struct W4 {
       // acc += s_n * (P - (128 + zp) * R); lane holds columns n = 4*og + r of each n-tile
       const int half = kt & 1;
       const uint32_t* sZ = (const uint32_t*)((const char*)sS + Cfg::S_BYTES);
+      auto correct = [&](auto with_z) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        float s[4], zo[4];
+        for (int tn = 0; tn < TN; ++tn) {
+          float s[4], zo[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t dw = sS[w * 64 + tn * 16 + 4 * og + r];
-          s[r] = f16_bits_to_f32((uint16_t)(half ? dw >> 16 : dw & 0xFFFF));
-          zo[r] = has_z ? 128.0f + (float)((sZ[w * 64 + tn * 16 + 4 * og + r] >> (8 * (kt & 3))) & 0xFFu) : zoff;
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t dw = sS[w * 64 + tn * 16 + 4 * og + r];
+            s[r] = f16_bits_to_f32((uint16_t)(half ? dw >> 16 : dw & 0xFFFF));
+            if constexpr (decltype(with_z)::value)
+              zo[r] = 128.0f + (float)((sZ[w * 64 + tn * 16 + 4 * og + r] >> (8 * (kt & 3))) & 0xFFu);
+            else
+              zo[r] = zoff;
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc.v[tn][mt][r] = __builtin_fmaf(s[r], __builtin_fmaf(-zo[r], R[mt][r], P[tn][mt][r]), acc.v[tn][mt][r]);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc.v[tn][mt][r] = __builtin_fmaf(s[r], __builtin_fmaf(-zo[r], R[mt][r], P[tn][mt][r]), acc.v[tn][mt][r]);
-      }
+      };
+      // uniform branch: the symmetric case reads no zero points
+      if (has_z)
+        correct(std::true_type{});
+      else
+        correct(std::false_type{});
     };
 
     const int nk = u.ke - u.kb;
