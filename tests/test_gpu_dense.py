@@ -209,3 +209,35 @@ def test_skinny_fp16_and_int8(g, ws):
         for kn in ("skinny_I8_1x16x32x256b_w4_d3_n0", "skinny_I8_1x16x128x256b_w8_d2_n1"):
             op = qg.operation(policy=qg.POLICY_FORCE, schedule=sched, split_k=8, programs=256, kernel=kidx(kn))
             check_against_oracle(p, Run(g, p, ws).run(op), what=f"skinny int8 decode {kn}")
+
+
+# ---------------------------------------------------------------- degenerate shapes
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_k_zero_gives_beta_c(g, ws, out):
+    # K = 0: the sum is empty, D = beta * C (alpha times an empty sum is 0)
+    M, N = 70, 136
+    C = synth.uniform((M, N), -2, 2, 3)
+    A = torch.empty(M, 0, device="cuda", dtype=torch.bfloat16)
+    B = torch.empty(N, 0, device="cuda", dtype=torch.bfloat16)
+    Cd_t = torch.from_numpy(C).cuda()
+    D = torch.full((M, N), float("nan"), device="cuda", dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    L = qg.layout
+    # a 16-byte-aligned dummy for the empty operands (never read)
+    dummy = torch.zeros(16, device="cuda", dtype=torch.bfloat16)
+    st = g.run_raw(qg.operation(), 2.0, dummy, L("bf16", M, 0, ld=8), None, None, dummy, L("bf16", N, 0, ld=8),
+                   None, None, -0.5, Cd_t, L("f32", M, N), D, L(out, M, N), ws.desc)
+    assert st == qg.OK
+    torch.cuda.synchronize()
+    want = torch.from_numpy(-0.5 * C.astype(np.float64))
+    got = D.double().cpu()
+    tol = 2.0 ** -8 * want.abs() + 1e-30 if out == "bf16" else 2.0 ** -23 * want.abs() + 1e-30
+    assert ((got - want).abs() <= tol).all()
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 16), (1, 8, 8), (3, 1, 64)])
+def test_tiny_edges(g, ws, shape):
+    M, N, K = shape
+    p = synth.dense_problem(M, N, K, "bf16", "f32", c_dtype="f32", alpha=1.0, beta=1.0, dist="uniform", seed=M + N + K)
+    r = Run(g, p, ws)
+    print(shape, r.plan(), flush=True)
+    check_against_oracle(p, r.run(), what=f"tiny {shape}")
