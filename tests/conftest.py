@@ -16,5 +16,10 @@ def pytest_sessionstart(session):
     # (the GPU machine receives them prebuilt).
     lib = os.path.join(ROOT, "quantized_gemm_bf16_amd", "libqgemm.so")
     if not os.path.exists(lib):
-        from quantized_gemm_bf16_amd import build as _b
-        _b.build()
+        # loaded by path: the package's own import needs the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_qg_build", os.path.join(ROOT, "quantized_gemm_bf16_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
+        b.build()
