@@ -146,7 +146,7 @@ struct Sched {
       Acc acc;
       Unit u = make_unit(a, t, 0, a.iters);
       Core::mainloop(a, u, smem, acc);
-      Core::store(a, u, acc);
+      Core::store(a, u, acc, smem);
     }
   }
 
@@ -161,7 +161,7 @@ struct Sched {
       if (arrive(a, u, t * a.splits + s, acc, flag)) {
         const int ns = (a.iters + a.iters_per_split - 1) / a.iters_per_split;
         reduce(a, ns, [&](int q) { return t * a.splits + q; }, acc);
-        Core::store(a, u, acc);
+        Core::store(a, u, acc, smem);
         finish_counter(a, u);
       }
     }
@@ -186,14 +186,14 @@ struct Sched {
         Unit u = make_unit(a, t, rem, rem + (end - it));
         Core::mainloop(a, u, smem, acc);
         if (rem == 0 && end - it == ipt) {
-          Core::store(a, u, acc);
+          Core::store(a, u, acc, smem);
         } else {
           const int slot = 2 * pid + (it == first_it ? 0 : 1);
           if (arrive(a, u, slot, acc, flag)) {
             const int t0 = t * ipt;
             const int plo = sk_owner(a, t0), phi = sk_owner(a, t0 + ipt - 1);
             reduce(a, phi - plo + 1, [&](int i) { return 2 * (plo + i) + (sk_start(a, plo + i) >= t0 ? 0 : 1); }, acc);
-            Core::store(a, u, acc);
+            Core::store(a, u, acc, smem);
             finish_counter(a, u);
           }
         }
@@ -206,7 +206,7 @@ struct Sched {
         Acc acc;
         Unit u = make_unit(a, t, 0, ipt);
         Core::mainloop(a, u, smem, acc);
-        Core::store(a, u, acc);
+        Core::store(a, u, acc, smem);
       }
     }
   }
@@ -258,7 +258,7 @@ struct Sched {
       u.ke = a.iters;
       Acc acc;
       Core::mainloop(a, u, smem, acc);
-      Core::store(a, u, acc);
+      Core::store(a, u, acc, smem);
     }
   }
 };

@@ -228,7 +228,7 @@ struct Skinny {
   }
 
   // Epilogue: wave 0 holds the tile (k-interleaved) or each wave its columns (N-split).
-  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc) {
+  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* /*smem*/) {
     if (!Cfg::NSPLIT && wave_id() != 0) return;
     const int l = lane_id();
     const int nw0 = Cfg::NSPLIT ? wave_id() * BNW : 0;

@@ -396,8 +396,75 @@ struct Tile {
     __syncthreads();  // the ring is reused by the next unit
   }
 
+  // Plain epilogue D = alpha * acc in a 16-bit type (no C, no fused steps):
+  // the MFMA layout leaves a lane 4 consecutive columns of one row, so stores
+  // straight from registers write 16-byte pieces of 32 different rows per
+  // instruction. Instead each wave stages its converted WTM x WTN tile in its
+  // own part of the (now idle) LDS ring and writes it back as whole row
+  // segments of WTN * 2 bytes. Staged rows keep 16-byte chunks under the same
+  // XOR key as the operand ring, so the 32 rows written by one instruction
+  // spread over the banks.
+  static constexpr int WROWB = Cfg::WTN * 2;  // bytes of one staged row
+  static constexpr int WCH = WROWB / 16;      // 16-byte chunks per staged row
+  static constexpr int WRPI = 64 / WCH;       // staged rows per 64-lane read
+  static constexpr bool STAGED = !Cfg::INT && WCH >= 4 && WCH <= 16 &&
+                                 Cfg::NW * Cfg::WTM * WROWB <= Cfg::STAGES * Cfg::STAGE_BYTES;
+  __device__ __forceinline__ static bool plain16(const Args& a) {
+    return (a.d_type == DT_BF16 || a.d_type == DT_F16) && (a.c_type < 0 || a.beta == 0.f) && a.epi == 0;
+  }
+
+  __device__ __forceinline__ static void store_staged(const Args& a, const Unit& u, Acc& acc, char* smem) {
+    const int w = wave_id(), l = lane_id();
+    const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
+    char* st = smem + w * (Cfg::WTM * WROWB);
+    const bool bf = a.d_type == DT_BF16;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int row = tm * 32 + (l & 31);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint16_t h[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = a.alpha * acc.v[tn][tm][4 * g + j];
+            h[j] = bf ? f32_to_bf16_bits(x) : f32_to_f16_bits(x);
+          }
+          const int ch = tn * 4 + g;
+          *(u16x4*)(st + row * WROWB + ((ch ^ swz<WCH>(row)) << 4) + 8 * (l >> 5)) = u16x4{h[0], h[1], h[2], h[3]};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done (lgkmcnt 0)
+    __builtin_amdgcn_wave_barrier();
+    const int ch = l % WCH;
+    const int n = u.n0 + wn * Cfg::WTN + ch * 8;
+#pragma unroll
+    for (int i = 0; i < Cfg::WTM / WRPI; ++i) {
+      const int row = i * WRPI + l / WCH;
+      const i32x4 v = *(const i32x4*)(st + row * WROWB + ((ch ^ swz<WCH>(row)) << 4));
+      const int64_t m = u.m0 + wm * Cfg::WTM + row;
+      if (m >= u.m_end || n >= a.N) continue;
+      uint16_t* p = (uint16_t*)a.D + m * a.ldd + n;
+      if (n + 8 <= a.N) {
+        *(i32x4*)p = v;
+      } else {
+        const uint16_t* hv = (const uint16_t*)&v;
+        for (int j = 0; j < 8; ++j)
+          if (n + j < a.N) p[j] = hv[j];
+      }
+    }
+    __syncthreads();  // the staging area is the next unit's ring
+  }
+
   // Final results of a tile: epilogue + masked store.
-  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc) {
+  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* smem) {
+    if constexpr (STAGED) {
+      if (plain16(a)) {
+        store_staged(a, u, acc, smem);
+        return;
+      }
+    }
     const int w = wave_id(), l = lane_id();
     const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
 #pragma unroll

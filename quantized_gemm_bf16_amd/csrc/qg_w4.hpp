@@ -206,7 +206,7 @@ struct W4 {
   }
 
   // Lane holds D[m][n .. n+3] with m = 16 mt + l%16, n = n0 + w*BNW + 16 tn + 4 (l/16).
-  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc) {
+  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* /*smem*/) {
     const int w = wave_id(), l = lane_id();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
