@@ -1,0 +1,17 @@
+// Explicit instantiations of the bf16 skinny kernels listed in qg_kernel_list.inc.
+#include "qg_skinny.hpp"
+
+namespace qg {
+#define QG_TILE_BF16(BM, BN, WM, WN, ST, RB)
+#define QG_TILE_F16(BM, BN, WM, WN, ST, RB)
+#define QG_TILE_I8(BM, BN, WM, WN, ST, RB)
+#define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS)
+#define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS)
+#define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS)
+#undef QG_SKINNY_BF16
+#define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) \
+  template hipError_t launch_skinny<SkinnyCfg<El::BF16, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
+#define QG_W4(BM, BN, NW, ST)
+#define QG_F8(BM, BN, WM, WN, ST)
+#include "qg_kernel_list.inc"
+}  // namespace qg
