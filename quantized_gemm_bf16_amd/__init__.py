@@ -5,7 +5,7 @@ descriptor structs, pass raw device pointers and the current HIP stream, and
 turn negative status codes into `QGemmError`. All arithmetic runs in the
 library's gfx950 kernels. PyTorch supplies device memory and streams.
 
-The library must have been built (`python -m quantized_gemm_bf16_amd.build`);
+The library must have been built (`python quantized_gemm_bf16_amd/build.py`);
 importing this package without it raises immediately -- there is no fallback.
 """
 from __future__ import annotations
@@ -70,7 +70,7 @@ class QGemmError(RuntimeError):
 
 def _load(path=LIB_PATH):
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m quantized_gemm_bf16_amd.build`")
+        raise ImportError(f"{path} is not built; run `python quantized_gemm_bf16_amd/build.py`")
     # PyTorch ships its own HIP runtime, asked for by file name (libamdhip64.so)
     # but carrying the soname libamdhip64.so.7 that libqgemm.so asks for. Loaded
     # first, it satisfies both; if libqgemm.so came first, torch would load a

@@ -2,7 +2,8 @@
 
 Every source under csrc/ is compiled on its own (in parallel) into _build/,
 then linked into quantized_gemm_bf16_amd/libqgemm.so. Usage:
-    python -m quantized_gemm_bf16_amd.build [--jobs N] [--save-temps]
+    python quantized_gemm_bf16_amd/build.py [--jobs N] [--save-temps]
+(run as a script: importing the package itself needs the built library)
 """
 from __future__ import annotations
 

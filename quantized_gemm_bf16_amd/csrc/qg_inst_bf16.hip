@@ -4,6 +4,7 @@
 
 namespace qg {
 #define QG_TILE_BF16(BM, BN, WM, WN, ST, RB)
+#define QG_TILE_BF16_BIG(BM, BN, WM, WN, ST, RB)
 #define QG_TILE_F16(BM, BN, WM, WN, ST, RB)
 #define QG_TILE_I8(BM, BN, WM, WN, ST, RB)
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS)

@@ -11,6 +11,7 @@ namespace qg {
 #define QG_DECL_SK(E, BN, NW, MT, DP, BB, NS) \
   extern template hipError_t launch_skinny<SkinnyCfg<El::E, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
 #define QG_TILE_BF16(BM, BN, WM, WN, ST, RB) QG_DECL(BF16, BM, BN, WM, WN, ST, RB)
+#define QG_TILE_BF16_BIG(BM, BN, WM, WN, ST, RB) QG_DECL(BF16, BM, BN, WM, WN, ST, RB)
 #define QG_TILE_F16(BM, BN, WM, WN, ST, RB) QG_DECL(F16, BM, BN, WM, WN, ST, RB)
 #define QG_TILE_I8(BM, BN, WM, WN, ST, RB) QG_DECL(I8, BM, BN, WM, WN, ST, RB)
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) QG_DECL_SK(BF16, BN, NW, MT, DP, BB, NS)
@@ -24,6 +25,7 @@ namespace qg {
 #undef QG_W4
 #undef QG_F8
 #undef QG_TILE_BF16
+#undef QG_TILE_BF16_BIG
 #undef QG_TILE_F16
 #undef QG_TILE_I8
 #undef QG_SKINNY_BF16
@@ -39,6 +41,7 @@ namespace qg {
    SkinnyCfg<El::E, BN, NW, MT, DP, BB, NS>::BK, DP, SkinnyCfg<El::E, BN, NW, MT, DP, BB, NS>::NT, 16 * MT * BN * 4,        \
    &launch_skinny<SkinnyCfg<El::E, BN, NW, MT, DP, BB, NS>>},
 #define QG_TILE_BF16(BM, BN, WM, WN, ST, RB) QG_ENTRY(BF16, DT_BF16, BM, BN, WM, WN, ST, RB)
+#define QG_TILE_BF16_BIG(BM, BN, WM, WN, ST, RB) QG_ENTRY(BF16, DT_BF16, BM, BN, WM, WN, ST, RB)
 #define QG_TILE_F16(BM, BN, WM, WN, ST, RB) QG_ENTRY(F16, DT_F16, BM, BN, WM, WN, ST, RB)
 #define QG_TILE_I8(BM, BN, WM, WN, ST, RB) QG_ENTRY(I8, DT_I8, BM, BN, WM, WN, ST, RB)
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(BF16, DT_BF16, BN, NW, MT, DP, BB, NS)
