@@ -9,7 +9,7 @@
 // Lmdeploy Gemm MainloopSm80V2": the scale advances once per group along K).
 //
 // Dequantisation in registers, before the MFMA, without rounding the weight:
-// a nibble q becomes the bf16 number 128 + q with one AND/OR (bf16 0x4300 is
+// a nibble q becomes the bf16 number 128 + q with one bitfield insert (bf16 0x4300 is
 // 128 and its last mantissa bit weighs 1), two nibbles per dword. Per group
 // the MFMA computes P = sum_k a_k (128 + q_k); a second MFMA against a column
 // of ones gives R = sum_k a_k; the group then adds
@@ -23,7 +23,7 @@
 // shared by the NW waves (wave w owns columns [w*BN/NW, (w+1)*BN/NW)). The
 // 128 k of a group map to MFMA k-slots as: step j, lane group g (lanes
 // 16g..16g+15) takes k 32g + 8j + {0,4,1,5,2,6,3,7}; A fragments are
-// byte-permuted into that order (v_perm), B comes out of the AND/OR in it.
+// byte-permuted into that order (v_perm), B comes out of the bitfield insert in it.
 #pragma once
 #include <type_traits>
 
@@ -50,6 +50,16 @@ struct W4Cfg {
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024 - 4096, "LDS budget");
   static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
 };
+
+// (x & 0x000F000F) | c for a c whose bits under the mask are zero: the two
+// nibbles at bits 0 and 16 of x become the low mantissa bits of two bf16
+// halves (v_bfi_b32 = (mask & x) | (~mask & c); the mask goes in an SGPR and c
+// in a VGPR, within gfx9's limit of one scalar operand per VALU instruction).
+__device__ __forceinline__ uint32_t nib_bf16(uint32_t x, uint32_t c) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(0x000F000Fu), "v"(x), "v"(c));
+  return d;
+}
 
 template <class Cfg>
 struct W4 {
@@ -112,6 +122,9 @@ struct W4 {
     };
 
     const int orow = l & 15, og = l >> 4;
+    // bf16 128.0 in both halves, kept in a VGPR for the bitfield insert
+    uint32_t c128;
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(c128));
     const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};  // bf16 1.0 pairs
     const float zoff = 128.0f + (float)a.zero_point;
 
@@ -153,10 +166,10 @@ struct W4 {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const uint32_t q = (uint32_t)bw[tn][j];
-          // bf16 pairs (128 + q_i, 128 + q_{i+4}) for i = 0..3
-          const i32x4 bq = {(int)((q & 0x000F000Fu) | 0x43004300u), (int)(((q >> 4) & 0x000F000Fu) | 0x43004300u),
-                            (int)(((q >> 8) & 0x000F000Fu) | 0x43004300u),
-                            (int)(((q >> 12) & 0x000F000Fu) | 0x43004300u)};
+          // bf16 pairs (128 + q_i, 128 + q_{i+4}) for i = 0..3: one bitfield
+          // insert per dword
+          const i32x4 bq = {(int)nib_bf16(q, c128), (int)nib_bf16(q >> 4, c128), (int)nib_bf16(q >> 8, c128),
+                            (int)nib_bf16(q >> 12, c128)};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) P[tn][mt] = mfma16_bf16(bq, af[mt], j == 0 ? f32x4{} : P[tn][mt]);
         }
