@@ -298,16 +298,26 @@ struct Tile {
     // Loads k-tile kt into ring stage `stage`; k-tiles outside [u.kb, u.ke)
     // (the ring runs STAGES tiles ahead) get an out-of-range offset, which
     // reads nothing and keeps the per-wave load count, and so vmcnt, uniform.
+    // A k-tile that lies wholly inside K (the usual case) takes the uniform
+    // branch without per-lane range selects.
     auto issue = [&](int stage, int kt) {
       char* sbase = smem + stage * Cfg::STAGE_BYTES;
       const uint32_t kk = (uint32_t)kt * ROWB;
       const bool live = kt < u.ke;
+      if (live && kk + ROWB <= kbytes) {
 #pragma unroll
-      for (int i = 0; i < Cfg::LA; ++i)
-        load_lds_x4(rA, sbase + (w * Cfg::LA + i) * 1024, live && kk + chA[i] < kbytes ? offA[i] + kk : kOOB);
+        for (int i = 0; i < Cfg::LA; ++i) load_lds_x4(rA, sbase + (w * Cfg::LA + i) * 1024, offA[i] + kk);
 #pragma unroll
-      for (int i = 0; i < Cfg::LB; ++i)
-        load_lds_x4(rB, sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024, live && kk + chB[i] < kbytes ? offB[i] + kk : kOOB);
+        for (int i = 0; i < Cfg::LB; ++i) load_lds_x4(rB, sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024, offB[i] + kk);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::LA; ++i)
+          load_lds_x4(rA, sbase + (w * Cfg::LA + i) * 1024, live && kk + chA[i] < kbytes ? offA[i] + kk : kOOB);
+#pragma unroll
+        for (int i = 0; i < Cfg::LB; ++i)
+          load_lds_x4(rB, sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024,
+                      live && kk + chB[i] < kbytes ? offB[i] + kk : kOOB);
+      }
     };
 
     // MFMA operand fragments of one k-step, read from LDS.
