@@ -47,6 +47,25 @@ def test_ragged_each_kernel(g, ws, kname, shape):
     check_against_oracle(p, r.run(op), what=f"{kname} {shape}")
 
 
+_TILES_16 = [n for n in qg.kernel_names() if n.startswith(("tile_BF16_", "tile_F16_"))]
+
+
+@pytest.mark.parametrize("kname", _TILES_16)
+@pytest.mark.parametrize("shape", [(300, 200, 136), (257, 517, 264), (33, 1001, 72), (1, 130, 8)])
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+def test_staged_epilogue_ragged(g, ws, kname, shape, out):
+    # 16-bit D with no C and no fused steps leaves through the LDS-staged
+    # row-segment store: ragged M and N tails (N % 8 != 0 takes the per-element
+    # end of a row), and nothing written past column N (checked by Run.run)
+    M, N, K = shape
+    ind = "f16" if kname.startswith("tile_F16_") else "bf16"
+    p = synth.dense_problem(M, N, K, ind, out, c_dtype=None, alpha=0.75, beta=0.0, dist="uniform", seed=M + 2 * N + K)
+    r = Run(g, p, ws)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname))
+    print(kname, shape, out, r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"{kname} {shape} {out}")
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("cdt", [None, "f32", "bf16", "f16"])
 def test_output_and_c_types(g, ws, out, cdt):
