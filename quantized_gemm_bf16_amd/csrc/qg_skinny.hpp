@@ -22,13 +22,16 @@
 
 namespace qg {
 
-// NSPLIT_ = false: the waves share the workgroup's BN columns and interleave
-// k-blocks (summed through LDS at the end); true: each wave owns BN / NW
-// columns over the whole k-range (no cross-wave sum).
-template <El E_, int BN_, int NW_, int MT_, int DEPTH_, int BLKB_ = 256, bool NSPLIT_ = false>
+// MODE_ 0: the waves share the workgroup's BN columns and interleave k-blocks
+// (summed through LDS at the end); 1: each wave owns BN / NW columns over the
+// whole k-range (no cross-wave sum); 2: as 1, but the A rows of a k-block are
+// loaded once per workgroup into a shared ring instead of once per wave (the
+// waves then meet at a barrier per block; a probe of the decode shape showed
+// the per-wave A reloads costing about 2.5 us of streaming time).
+template <El E_, int BN_, int NW_, int MT_, int DEPTH_, int BLKB_ = 256, int MODE_ = 0>
 struct SkinnyCfg {
   static constexpr El E = E_;
-  static constexpr bool NSPLIT = NSPLIT_;
+  static constexpr bool NSPLIT = MODE_ >= 1, SHARED_A = MODE_ == 2;
   static constexpr int BN = BN_, NW = NW_, MT = MT_, DEPTH = DEPTH_;
   static constexpr int BNW = NSPLIT ? BN / NW : BN;  // columns per wave
   static constexpr int NT = NW * 64, BM = 16 * MT, TN = BNW / 16;
@@ -38,11 +41,18 @@ struct SkinnyCfg {
   static constexpr int RPI = 64 / CPR;            // rows filled by one 64-lane load
   static constexpr int STEPS = BLKB / 64;         // MFMA k-steps per block
   static constexpr int BK = BLKB / ESIZE;         // k elements per block
-  static constexpr int SLOT = (BNW + BM) * BLKB;  // LDS bytes of one wave's ring slot
-  static constexpr int LPS = (BNW + BM) / RPI;    // 64-lane loads per slot
+  // LDS bytes of one wave's ring slot (B rows, plus its own A rows unless shared)
+  static constexpr int SLOT = (BNW + (SHARED_A ? 0 : BM)) * BLKB;
+  static constexpr int ASLOT = SHARED_A ? BM * BLKB : 0;  // one slot of the shared A ring
+  static constexpr int LA_SH = BM / RPI;                  // 64-lane loads of one shared A block
+  // 64-lane loads per slot and wave (shared A: one A load per wave, waves
+  // w and w + LA_SH repeating the same one)
+  static constexpr int LPS = SHARED_A ? BNW / RPI + 1 : (BNW + BM) / RPI;
+  static constexpr int LDS_BYTES = NW * DEPTH * SLOT + DEPTH * ASLOT;
   static_assert(BLKB == 256 || BLKB == 512 || BLKB == 1024, "block bytes");
-  static_assert(NW * DEPTH * SLOT <= 160 * 1024 - 4096, "LDS budget");
+  static_assert(LDS_BYTES <= 160 * 1024 - 4096, "LDS budget");
   static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
+  static_assert(!SHARED_A || (DEPTH >= 2 && LA_SH <= NW), "shared A ring");
   static constexpr bool INT = (E_ == El::I8);
   static_assert(BNW % 16 == 0 && BNW * (NSPLIT ? NW : 1) == BN && DEPTH >= 1, "skinny tile");
 };
@@ -62,7 +72,7 @@ struct Skinny {
   using S4 = typename AccOf<Cfg::INT>::S4;
   static constexpr int TN = Cfg::TN, MT = Cfg::MT, NW = Cfg::NW, DEPTH = Cfg::DEPTH;
   static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, BNW = Cfg::BNW;
-  static constexpr int SMEM_BYTES = NW * DEPTH * Cfg::SLOT;  // per-wave rings (reused for the reduction)
+  static constexpr int SMEM_BYTES = Cfg::LDS_BYTES;  // per-wave rings (+ shared A ring; reused for the reduction)
   static_assert(NW * TN * MT * 64 * 16 <= SMEM_BYTES, "reduction space");
   // v: accumulators; c: this lane's C values, loaded when the unit starts so
   // that the epilogue does not wait for them at the end of the stream
@@ -98,6 +108,10 @@ struct Skinny {
   }
 
   __device__ __forceinline__ static void mainloop(const Args& a, const Unit& u, char* smem, Acc& acc) {
+    if constexpr (Cfg::SHARED_A) {
+      mainloop_shared_a(a, u, smem, acc);
+      return;
+    }
     const int w = wave_id(), l = lane_id();
     constexpr int ES = Cfg::ESIZE;
     const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
@@ -225,6 +239,99 @@ struct Skinny {
           for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] += red[((w2 * TN + tn) * MT + mt) * 64 + l];
     }
     __syncthreads();
+  }
+
+  // N-split with a shared A ring: wave w keeps a private DEPTH-slot ring of
+  // its B rows; the A rows of each block go to a workgroup ring (load i of
+  // the LA_SH 1 KB loads of a block is issued by waves i, i + LA_SH, ...:
+  // the repeats write the same bytes to the same place and keep every
+  // wave's load count, and so vmcnt, uniform). Per block: wait for this
+  // wave's loads of block b, meet (so every wave's part of A(b) has landed
+  // and every wave is done reading block b - 1), refill block b - 1's slots
+  // with block b + DEPTH - 1, read block b, compute. DEPTH - 1 blocks stay
+  // in flight behind the one being consumed; the summation order per
+  // output is that of MODE 1, so results are identical.
+  __device__ __forceinline__ static void mainloop_shared_a(const Args& a, const Unit& u, char* smem, Acc& acc) {
+    const int w = wave_id(), l = lane_id();
+    constexpr int ES = Cfg::ESIZE, CPR = Cfg::CPR, RPI = Cfg::RPI, LB = BNW / RPI, ST = Cfg::STEPS;
+    const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
+    const uint32_t kbytes = (uint32_t)a.K * ES;
+    const int a_rows = max(0, min(BM, u.m_end - u.m0));
+    const int b_rows = max(0, min(BN, a.N - u.n0));
+    const i32x4 rA = make_rsrc_words((const char*)a.A + (int64_t)u.m0 * lda_b, (uint32_t)(a_rows * lda_b));
+    const int nw0 = w * BNW;
+    const int b_rows_w = max(0, min(BNW, b_rows - nw0));
+    const i32x4 rB = make_rsrc_words((const char*)a.B + (int64_t)u.expert * a.b_batch * ES + (int64_t)(u.n0 + nw0) * ldb_b,
+                                     (uint32_t)(b_rows_w * ldb_b));
+    char* bring = smem + w * DEPTH * Cfg::SLOT;
+    char* aring = smem + NW * DEPTH * Cfg::SLOT;
+    const int lrow = l / CPR;
+    uint32_t offB[LB], chB[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = i * RPI + lrow;
+      chB[i] = (uint32_t)(((l % CPR) ^ (row & 15)) * 16);
+      offB[i] = (uint32_t)(row * ldb_b) + chB[i];
+    }
+    const int ia = w % Cfg::LA_SH;
+    const int arow = ia * RPI + lrow;
+    const uint32_t chA = (uint32_t)(((l % CPR) ^ (arow & 15)) * 16);
+    const uint32_t offA = (uint32_t)(arow * lda_b) + chA;
+    auto issue = [&](int d, int blk) {
+      char* base = bring + d * Cfg::SLOT;
+      const bool live = blk < u.ke;
+      const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
+#pragma unroll
+      for (int i = 0; i < LB; ++i) load_lds_x4(rB, base + i * 1024, live && kk + chB[i] < kbytes ? offB[i] + kk : kOOB);
+      load_lds_x4(rA, aring + d * Cfg::ASLOT + ia * 1024, live && kk + chA < kbytes ? offA + kk : kOOB);
+    };
+    i32x4 fb[ST][TN], fa[ST][MT];
+    auto read = [&](int d) {
+      const char* bb = bring + d * Cfg::SLOT;
+      const char* ab = aring + d * Cfg::ASLOT;
+#pragma unroll
+      for (int j = 0; j < ST; ++j) {
+        const int c = 4 * j + (l >> 4);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int row = tn * 16 + (l & 15);
+          fb[j][tn] = *(const i32x4*)(bb + row * Cfg::BLKB + ((c ^ (row & 15)) << 4));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int row = mt * 16 + (l & 15);
+          fa[j][mt] = *(const i32x4*)(ab + row * Cfg::BLKB + ((c ^ (row & 15)) << 4));
+        }
+      }
+    };
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = S4{};
+    prefetch_c(a, u, acc);
+    const int nk = u.ke - u.kb;
+    // rounded up to whole rounds of DEPTH blocks: blocks past the unit read
+    // nothing (zeros) and add nothing
+    const int rounds = (nk + DEPTH - 1) / DEPTH;
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) issue(d, u.kb + d);
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        wait_vmcnt<Cfg::LPS * (DEPTH - 2)>();
+        lds_barrier();
+        issue((d + DEPTH - 1) % DEPTH, u.kb + r * DEPTH + d + DEPTH - 1);
+        read(d);
+#pragma unroll
+        for (int j = 0; j < ST; ++j)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = mma(fb[j][tn], fa[j][mt], acc.v[tn][mt]);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // the rings are reused by the next unit
   }
 
   // Epilogue: wave 0 holds the tile (k-interleaved) or each wave its columns (N-split).

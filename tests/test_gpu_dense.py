@@ -185,7 +185,7 @@ def test_tiny_config_plan_is_logged(g, ws):
 
 # ---------------------------------------------------------------- skinny-M streaming kernels
 SKINNY = ["skinny_BF16_1x16x16x256b_w4_d4_n0", "skinny_BF16_1x16x128x256b_w8_d2_n1", "skinny_BF16_1x16x64x256b_w2_d2_n0",
-          "skinny_BF16_2x16x32x256b_w4_d2_n0", "skinny_BF16_1x16x64x256b_w4_d3_n1"]
+          "skinny_BF16_2x16x32x256b_w4_d2_n0", "skinny_BF16_1x16x64x256b_w4_d3_n1", "skinny_BF16_1x16x128x256b_w8_d3_n2"]
 
 
 @pytest.mark.parametrize("kname", SKINNY)
@@ -217,6 +217,31 @@ def test_skinny_decode_full_size_split8(g, ws, M):
     op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8, kernel=kidx("skinny_BF16_1x16x32x256b_w4_d3_n0"))
     print(r.plan(op), flush=True)
     check_against_oracle(p, r.run(op), what=f"skinny decode M={M}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_skinny_shared_a_ring_matches_per_wave_a(g, ws, dt):
+    # the shared-A N-split kernel sums every output in the same order as the
+    # per-wave-A one: bit-identical results, at the decode shape with split-K 8
+    p = synth.dense_problem(16, 4096, 14336, dt, dt, c_dtype=dt, alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02, seed=21)
+    r = Run(g, p, ws)
+    E = "BF16" if dt == "bf16" else "F16"
+    out = {}
+    for kn in (f"skinny_{E}_1x16x128x256b_w8_d3_n2", f"skinny_{E}_1x16x128x256b_w8_d2_n1"):
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8, kernel=kidx(kn))
+        print(kn, r.plan(op), flush=True)
+        out[kn] = r.run(op)
+    a, b = out.values()
+    check_against_oracle(p, a, rows=sample_rows(16, 4), what=f"shared-A decode {dt}")
+    assert np.array_equal(a, b)
+    assert int(ws.barriers.abs().sum().item()) == 0
+
+
+def test_decode_default_plan_uses_shared_a(g, ws):
+    p = synth.config_decode(M=16)
+    r = Run(g, p, ws)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    assert "kernel=skinny_BF16_1x16x128x256b_w8_d3_n2" in r.plan(op)
 
 
 def test_skinny_fp16_and_int8(g, ws):
