@@ -237,6 +237,22 @@ def test_skinny_shared_a_ring_matches_per_wave_a(g, ws, dt):
     assert int(ws.barriers.abs().sum().item()) == 0
 
 
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("sched", ["split8", "streamk256"])
+def test_decode_full_size_default_kernels(g, ws, M, sched):
+    # the decode configuration exactly as the benchmark runs it (kernel left to
+    # the heuristic), every output against the oracle
+    p = synth.config_decode(M=M)
+    r = Run(g, p, ws)
+    if sched == "split8":
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+    else:
+        op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=256)
+    print(M, sched, r.plan(op), flush=True)
+    check_against_oracle(p, r.run(op), what=f"decode M={M} {sched}")
+    assert int(ws.barriers.abs().sum().item()) == 0
+
+
 def test_decode_default_plan_uses_shared_a(g, ws):
     p = synth.config_decode(M=16)
     r = Run(g, p, ws)
