@@ -147,7 +147,7 @@ def main():
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the engine runs on a single device).", file=sys.stderr)
         return 2
 
