@@ -265,6 +265,26 @@ int qg_kernel_count(void);
 /* Name of registry entry `index`, or NULL when out of range. */
 const char* qg_kernel_name(int index);
 
+/* ---- schedule introspection ---------------------------------------------- */
+/* The stream-K division that QG_SCHED_STREAMK runs for `tiles` output tiles
+ * of `iters` k-iterations each on `programs` programs (the work-sharing idea
+ * of the TileLang tutorial page "gemm_variants.py", gemm_streamk; the split
+ * itself is this library's: whole tiles round-robin first, then the last
+ * P + T % P tiles' k-iterations (all tiles when T < P; none when P divides T)
+ * in P contiguous balanced ranges, program p owning
+ * [floor(p W / P), floor((p + 1) W / P)) of their W iterations).
+ * qg_streamk_units writes, for every program in order, its work units as rows
+ * of five int32 (program, tile, k_begin, k_end, slot) in execution order;
+ * slot is the partials-workspace slot of a partial piece, -1 for a whole tile
+ * stored directly. At most `cap` rows are written; *count receives the total
+ * (QG_ERR_BUFFER_SMALL when it exceeds cap). Host-only, computed by the same
+ * code the kernels run. */
+int qg_streamk_units(int tiles, int iters, int programs, int32_t* rows, int cap, int* count);
+/* The order in which the workgroup completing shared tile `tile` sums its
+ * partial pieces: the slots of the owning programs' pieces in k order
+ * (*count = 0 for a tile taken whole). Same conventions as above. */
+int qg_streamk_fixup(int tiles, int iters, int programs, int tile, int32_t* slots, int cap, int* count);
+
 /* Static text for a status code. */
 const char* qg_status_str(int status);
 /* Library version string. */

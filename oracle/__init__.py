@@ -9,15 +9,11 @@ path. It holds
     `oracle.c` (D = alpha*(A@B) + beta*C, the operation of the page
     "InternLM Lmdeploy Gemm Interface", Description / Run signature),
     returning (ref, absdot) for every requested output;
-  * the scalar decoders of that library (bf16, fp16, OCP E4M3);
-  * `streamk_plan` / `streamk_segments`: the stream-K work division of the
-    TileLang tutorial page "gemm_variants.py" (functions streamk_plan and
-    gemm_streamk), restated: a fixed number of programs split the
-    stream-K tiles' k-iterations evenly, the leftover "blocking" tiles are
-    taken whole, round-robin. One reading is added where the page is wrong:
-    a blocking tile id at or past the tile count is skipped (the page's
-    `max(blocking_tiles // total_sm, 1)` makes programs visit a tile that
-    does not exist when there are no blocking tiles).
+  * the scalar decoders of that library (bf16, fp16, OCP E4M3).
+
+How work is divided among workgroups (split-K, stream-K) does not change
+what is computed, so the oracle has no notion of it beyond the `splits`
+self-check (contiguous K chunks summed in fp64, then in order).
 """
 from __future__ import annotations
 
@@ -234,53 +230,3 @@ def quant_codes(p: dict, ref, rows=None):
         raise ValueError("oracle rejected the problem")
     return pre, code
 
-
-# ---------------------------------------------------------------------------
-# stream-K work division (TileLang tutorial "gemm_variants.py": streamk_plan,
-# gemm_streamk)
-# ---------------------------------------------------------------------------
-def streamk_plan(m, n, k, block_m, block_n, block_k, programs):
-    """The plan's size parameters. The stream-K tiles are the remainder of the
-    tile count over the program count, plus one more full round when more than
-    one round would otherwise be left to the blocking phase; their k-iterations
-    are shared out evenly (`full` each, the first `partial` programs one more)."""
-    tiles_m = math.ceil(m / block_m)
-    tiles_n = math.ceil(n / block_n)
-    ipt = math.ceil(k / block_k)
-    total = tiles_m * tiles_n
-    sk_tiles = total % programs
-    if total - sk_tiles > programs:
-        sk_tiles += programs
-    blocking = total - sk_tiles
-    sk_iters = sk_tiles * ipt
-    return {
-        "iters_per_tile": ipt,
-        "total_tiles": total,
-        "streamk_tiles": sk_tiles,
-        "blocking_tiles": blocking,
-        "full_tiles": sk_iters // programs,
-        "partial_tiles": sk_iters % programs,
-        "sm_partition_factor": max(blocking // programs, 1),
-    }
-
-
-def streamk_segments(m, n, k, block_m, block_n, block_k, programs):
-    """Every (program, tile, k_iter_begin, k_iter_end) the plan produces: the
-    program's contiguous share of stream-K iterations cut at tile boundaries,
-    then its blocking tiles (tile ids past the tile count skipped)."""
-    pl = streamk_plan(m, n, k, block_m, block_n, block_k, programs)
-    ipt, full, part = pl["iters_per_tile"], pl["full_tiles"], pl["partial_tiles"]
-    out = []
-    for pid in range(programs):
-        it = pid * full + min(pid, part)
-        last = (pid + 1) * full + min(pid + 1, part)
-        while it < last:
-            tile = it // ipt
-            end = min(it + (ipt - it % ipt), last)
-            out.append((pid, tile, it % ipt, it % ipt + (end - it)))
-            it = end
-        for r in range(pl["sm_partition_factor"]):
-            tile = pid + pl["streamk_tiles"] + r * programs
-            if tile < pl["total_tiles"]:
-                out.append((pid, tile, 0, ipt))
-    return out

@@ -32,7 +32,7 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3, "i8": I8, "i3
 
 EXPORTS = ["qg_create", "qg_destroy", "qg_barriers_size", "qg_partials_size", "qg_run", "qg_plan",
            "qg_export", "qg_import", "qg_get_tuning_seq", "qg_cache_size", "qg_kernel_count",
-           "qg_kernel_name", "qg_status_str", "qg_version"]
+           "qg_kernel_name", "qg_status_str", "qg_version", "qg_streamk_units", "qg_streamk_fixup"]
 
 
 class Layout(ctypes.Structure):
@@ -97,8 +97,10 @@ def _load(path=LIB_PATH):
     L.qg_status_str.argtypes = [i32]
     L.qg_status_str.restype = ctypes.c_char_p
     L.qg_version.restype = ctypes.c_char_p
+    L.qg_streamk_units.argtypes = [i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
+    L.qg_streamk_fixup.argtypes = [i32, i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
     for name in ("qg_create", "qg_destroy", "qg_run", "qg_plan", "qg_export", "qg_import",
-                 "qg_get_tuning_seq", "qg_cache_size"):
+                 "qg_get_tuning_seq", "qg_cache_size", "qg_streamk_units", "qg_streamk_fixup"):
         getattr(L, name).restype = i32
     return L
 
@@ -124,6 +126,27 @@ def partials_size() -> int:
 
 def kernel_names():
     return [lib.qg_kernel_name(i).decode() for i in range(lib.qg_kernel_count())]
+
+
+def streamk_units(tiles, iters, programs):
+    """qg_streamk_units: [(program, tile, k_begin, k_end, slot), ...]."""
+    n = ctypes.c_int()
+    st = lib.qg_streamk_units(int(tiles), int(iters), int(programs), None, 0, ctypes.byref(n))
+    if st not in (OK, ERR_BUFFER_SMALL):
+        raise QGemmError(st, "qg_streamk_units")
+    buf = (ctypes.c_int32 * (5 * max(n.value, 1)))()
+    _check(lib.qg_streamk_units(int(tiles), int(iters), int(programs), buf, n.value, ctypes.byref(n)),
+           "qg_streamk_units")
+    return [tuple(buf[5 * i:5 * i + 5]) for i in range(n.value)]
+
+
+def streamk_fixup(tiles, iters, programs, tile):
+    """qg_streamk_fixup: partial-piece slots of a shared tile in k order."""
+    buf = (ctypes.c_int32 * (programs + 1))()
+    n = ctypes.c_int()
+    _check(lib.qg_streamk_fixup(int(tiles), int(iters), int(programs), int(tile), buf, programs + 1,
+                                ctypes.byref(n)), "qg_streamk_fixup")
+    return list(buf[:n.value])
 
 
 def layout(dtype, rows, cols, ld=None, num=0, offsets=0, stride=0, order=ROW_MAJOR) -> Layout:
@@ -185,6 +208,7 @@ class Gemm:
 
     def run(self, *args, **kw):
         _check(self.run_raw(*args, **kw), "qg_run")
+
 
     def plan(self, op, Ad, Ud, Bd, Vd, Cd, Dd, alpha, beta, ws=None) -> str:
         buf = ctypes.create_string_buffer(512)

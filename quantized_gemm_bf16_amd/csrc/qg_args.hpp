@@ -42,7 +42,9 @@ struct Args {
   int32_t tiles_m, tiles_n;  // DP/split/stream: exact; grouped: tiles_n only
   int32_t iters;             // k-iterations (k-tiles) per output tile
   int32_t splits, iters_per_split;
-  int32_t programs, sk_tiles, sk_full, sk_partial, dp_rounds;
+  int32_t programs;          // stream-K: programs (one per workgroup)
+  int32_t dp_tiles;          // stream-K: leading tiles taken whole, round-robin
+  int32_t sk_work;           // stream-K: k-iterations of the remaining tiles, shared evenly
   int32_t group_m;           // tile-order super-group height (in tiles)
   int32_t grid;              // workgroups launched
   int32_t* counters;         // barriers workspace: one int32 per output tile

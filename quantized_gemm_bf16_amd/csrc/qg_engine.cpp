@@ -18,11 +18,13 @@
 #include <mutex>
 #include <sstream>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/qgemm.h"
 #include "qg_args.hpp"
 #include "qg_registry.hpp"
+#include "qg_streamk.hpp"
 
 using namespace qg;
 
@@ -119,6 +121,30 @@ struct Plan {
 
 }  // namespace
 
+namespace {
+
+// Memo of resolved DEFAULT-policy choices, keyed by everything the cache
+// lookup and the heuristic read (exact M, problem key fields, workspace
+// sizes). It turns a repeated call into one hash lookup instead of
+// formatting text keys and probing the tuning-sequence buckets; any change to
+// the cache (measure, import) clears it.
+struct MemoKey {
+  int64_t M, N, K;
+  int32_t ta, tb, tc, td, qa, qb, E, batched, epi, pad;
+  uint64_t ws_partials, ws_barriers;
+  bool operator==(const MemoKey& o) const { return memcmp(this, &o, sizeof o) == 0; }
+};
+struct MemoHash {
+  size_t operator()(const MemoKey& k) const {
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(&k);
+    uint64_t h = 1469598103934665603ull;  // FNV-1a
+    for (size_t i = 0; i < sizeof k; ++i) h = (h ^ b[i]) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+
+}  // namespace
+
 struct qg_handle {
   int device = -1;
   int cus = 256;
@@ -126,6 +152,7 @@ struct qg_handle {
   bool online = false;
   std::mutex mu;
   std::map<std::string, Entry> cache;  // key: "<M>|<problem key>"
+  std::unordered_map<MemoKey, Choice, MemoHash> memo;
 };
 
 namespace {
@@ -443,21 +470,17 @@ int make_plan(const qg_handle* h, const Problem& p, const Choice& c, const qg_wo
       }
     } else if (mode == MODE_STREAMK) {
       const int P = c.programs > 0 ? c.programs : h->cus;
-      const int64_t total = tiles;
-      int64_t sk = total % P;
-      if (total - sk > P) sk += P;
-      const int64_t blocking = total - sk;
-      const int64_t sk_iters = sk * a.iters;
+      // the device arithmetic runs in 32 bits (qg_streamk.hpp)
+      if (P > kStreamKMaxPrograms || tiles * a.iters > INT32_MAX) return QG_ERR_UNSUPPORTED;
+      const StreamK sk = StreamK::make((int)tiles, a.iters, P);
       a.programs = P;
-      a.sk_tiles = (int32_t)sk;
-      a.sk_full = (int32_t)(sk_iters / P);
-      a.sk_partial = (int32_t)(sk_iters % P);
-      a.dp_rounds = (int32_t)std::max<int64_t>(blocking / P, 1);
+      a.dp_tiles = sk.dp_tiles;
+      a.sk_work = sk.work;
       pl.c.programs = P;
       pl.c.split = 1;
       pl.grid = P;
       pl.partials = (size_t)2 * P * k.slot_bytes;
-      pl.barriers = (size_t)total * 4;
+      pl.barriers = (size_t)tiles * 4;
     } else {
       return QG_ERR_INVALID_ARG;
     }
@@ -720,8 +743,23 @@ int measure(qg_handle* h, const Problem& p, const qg_workspace* ws, hipStream_t 
   en.c = best;
   en.us = best_us;
   h->cache[cache_key(p.M, p.key())] = en;
+  h->memo.clear();
   return QG_OK;
 }
+
+MemoKey memo_key(const Problem& p, const qg_workspace* ws) {
+  MemoKey k;
+  memset(&k, 0, sizeof k);
+  k.M = p.M, k.N = p.N, k.K = p.K;
+  k.ta = p.ta, k.tb = p.tb, k.tc = p.tc, k.td = p.td, k.qa = p.qa, k.qb = p.qb;
+  k.E = p.E, k.batched = p.batched, k.epi = p.epi;
+  const bool ws_ok = ws && ws->partials && ws->barriers;
+  k.ws_partials = ws_ok ? ws->partials_size : 0;
+  k.ws_barriers = ws_ok ? ws->barriers_size : 0;
+  return k;
+}
+
+constexpr size_t kMemoMax = 4096;
 
 // Resolves the plan for a run (shared by qg_run and qg_plan).
 int resolve(qg_handle* h, const qg_operation* op, const Problem& p, const qg_workspace* ws, Plan& pl,
@@ -748,16 +786,43 @@ int resolve(qg_handle* h, const qg_operation* op, const Problem& p, const qg_wor
       return make_plan(h, p, c, ws, pl);
     case QG_POLICY_MEASURE:
       if (allow_measure && !lookup(h, p, c, true)) {
-        int st = measure(h, p, ws, s, c);
-        if (st != QG_OK) return st;
-        return make_plan(h, p, c, ws, pl);
+        // Measuring synchronises the stream, which a stream being captured
+        // into a graph does not allow: while capturing, resolve as DEFAULT
+        // (cache, else heuristic) and leave the measurement to a later call.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+          (void)hipGetLastError();
+          return QG_ERR_HIP;
+        }
+        if (cs == hipStreamCaptureStatusNone) {
+          int st = measure(h, p, ws, s, c);
+          if (st != QG_OK) return st;
+          return make_plan(h, p, c, ws, pl);
+        }
       }
       // fallthrough
     case QG_POLICY_DEFAULT: {
-      if (lookup(h, p, c, false) && make_plan(h, p, c, ws, pl) == QG_OK) return QG_OK;
-      c = heuristic(h, p, ws);
-      if (c.kernel < 0) return QG_ERR_NO_KERNEL;
-      return make_plan(h, p, c, ws, pl);
+      const MemoKey mk = memo_key(p, ws);
+      bool hit = false;
+      {
+        std::lock_guard<std::mutex> g(h->mu);
+        auto it = h->memo.find(mk);
+        if (it != h->memo.end()) {
+          c = it->second;
+          hit = true;
+        }
+      }
+      if (hit && make_plan(h, p, c, ws, pl) == QG_OK) return QG_OK;
+      if (!(lookup(h, p, c, false) && make_plan(h, p, c, ws, pl) == QG_OK)) {
+        c = heuristic(h, p, ws);
+        if (c.kernel < 0) return QG_ERR_NO_KERNEL;
+        const int st = make_plan(h, p, c, ws, pl);
+        if (st != QG_OK) return st;
+      }
+      std::lock_guard<std::mutex> g(h->mu);
+      if (h->memo.size() >= kMemoMax) h->memo.clear();
+      h->memo[mk] = c;
+      return QG_OK;
     }
     default:
       return QG_ERR_INVALID_ARG;
@@ -920,6 +985,7 @@ int qg_import(qg_handle* h, const char* buf, size_t len) {
     if (got != n) return QG_ERR_FORMAT;
     std::lock_guard<std::mutex> g(h->mu);
     for (auto& kv : staged) h->cache[kv.first] = kv.second;
+    h->memo.clear();
   }
   return QG_OK;
 }
@@ -937,6 +1003,43 @@ int qg_cache_size(qg_handle* h, int* count) {
   std::lock_guard<std::mutex> g(h->mu);
   *count = (int)h->cache.size();
   return QG_OK;
+}
+
+int qg_streamk_units(int tiles, int iters, int programs, int32_t* rows, int cap, int* count) {
+  if (tiles < 0 || iters < 1 || programs < 1 || cap < 0 || !count || (cap > 0 && !rows)) return QG_ERR_INVALID_ARG;
+  if (programs > kStreamKMaxPrograms || (int64_t)tiles * iters > INT32_MAX) return QG_ERR_UNSUPPORTED;
+  const StreamK sk = StreamK::make(tiles, iters, programs);
+  int n = 0;
+  for (int p = 0; p < programs; ++p) {
+    StreamKCursor cur(sk, p);
+    int t, kb, ke, slot;
+    while (cur.next(t, kb, ke, slot)) {
+      if (n < cap) {
+        int32_t* r = rows + 5 * (int64_t)n;
+        r[0] = p, r[1] = t, r[2] = kb, r[3] = ke, r[4] = slot;
+      }
+      ++n;
+    }
+  }
+  *count = n;
+  return n > cap ? QG_ERR_BUFFER_SMALL : QG_OK;
+}
+
+int qg_streamk_fixup(int tiles, int iters, int programs, int tile, int32_t* slots, int cap, int* count) {
+  if (tiles < 1 || iters < 1 || programs < 1 || tile < 0 || tile >= tiles || cap < 0 || !count ||
+      (cap > 0 && !slots))
+    return QG_ERR_INVALID_ARG;
+  if (programs > kStreamKMaxPrograms || (int64_t)tiles * iters > INT32_MAX) return QG_ERR_UNSUPPORTED;
+  const StreamK sk = StreamK::make(tiles, iters, programs);
+  if (tile < sk.dp_tiles) {
+    *count = 0;
+    return QG_OK;
+  }
+  const int w0 = (tile - sk.dp_tiles) * iters;
+  const int n = sk.pieces(w0);
+  for (int i = 0; i < n && i < cap; ++i) slots[i] = sk.piece_slot(w0, i);
+  *count = n;
+  return n > cap ? QG_ERR_BUFFER_SMALL : QG_OK;
 }
 
 int qg_kernel_count(void) { return kNumKernels; }

@@ -175,7 +175,13 @@ struct F8 : Tile<Cfg> {
           for (int r = 0; r < 16; ++r) acc.v[tn][tm][r] = __builtin_fmaf(f, t[tn][tm][r], acc.v[tn][tm][r]);
         }
     }
-    __syncthreads();  // the ring is reused by the next unit
+    // The last k-steps issued loads for k-tiles past the unit (out-of-range
+    // offsets, which still write zeros into the ring). The compiler does not
+    // count these inline-assembly loads, so __syncthreads() alone would not
+    // wait for them: wait explicitly before the ring is reused (staged
+    // epilogue, next unit's prologue).
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 };
 

@@ -9,11 +9,9 @@
 //   DP       one unit = one whole tile; with one workgroup per tile the block
 //            id is remapped so each XCD (own L2) gets a contiguous range.
 //   SPLITK   tile t, chunk s: k-tiles [s*ips, min(iters, (s+1)*ips)).
-//   STREAMK  program p takes the contiguous k-iterations
-//            [p*full + min(p, partial), (p+1)*full + min(p+1, partial)) of the
-//            stream-K tiles, cut at tile boundaries, then whole "blocking"
-//            tiles round-robin (TileLang tutorial "gemm_variants.py",
-//            gemm_streamk / streamk_plan; tile ids past the count skipped).
+//   STREAMK  program p takes its whole tiles round-robin, then a balanced
+//            contiguous range of the remaining tiles' k-iterations, cut at
+//            tile boundaries (qg_streamk.hpp).
 //   GROUPED  persistent loop over the tiles of all experts, found from the
 //            device offsets array (tutorial function gemm_grouped: padded
 //            per-expert m-block prefix; rows past an expert's end masked).
@@ -28,6 +26,7 @@
 #pragma once
 #include "qg_args.hpp"
 #include "qg_device.hpp"
+#include "qg_streamk.hpp"
 
 namespace qg {
 
@@ -167,46 +166,33 @@ struct Sched {
     }
   }
 
-  __device__ __forceinline__ static int sk_start(const Args& a, int p) { return p * a.sk_full + min(p, a.sk_partial); }
-  __device__ __forceinline__ static int sk_owner(const Args& a, int it) {
-    const int big = a.sk_partial * (a.sk_full + 1);
-    return it < big ? it / (a.sk_full + 1) : a.sk_partial + (it - big) / a.sk_full;
-  }
-
+  // Stream-K (qg_streamk.hpp): whole tiles first, then the program's
+  // balanced range of the shared region; a tile's partial pieces are summed
+  // in k order by the workgroup that completes it.
   __device__ __forceinline__ static void run_streamk(const Args& a, char* smem, int* flag) {
-    const int ipt = a.iters;
+    StreamK sk;
+    sk.tiles = a.tiles_m * a.tiles_n;
+    sk.iters = a.iters;
+    sk.programs = a.programs;
+    sk.dp_tiles = a.dp_tiles;
+    sk.work = a.sk_work;
+    sk.f = a.sk_work / a.programs;
+    sk.r = a.sk_work % a.programs;
     for (int pid = blockIdx.x; pid < a.programs; pid += gridDim.x) {
-      int it = sk_start(a, pid);
-      const int last = sk_start(a, pid + 1);
-      const int first_it = it;
-      while (it < last) {
-        const int t = it / ipt, rem = it - t * ipt;
-        const int end = min(it + (ipt - rem), last);
+      StreamKCursor cur(sk, pid);
+      int t, kb, ke, slot;
+      while (cur.next(t, kb, ke, slot)) {
         Acc acc;
-        Unit u = make_unit(a, t, rem, rem + (end - it));
+        Unit u = make_unit(a, t, kb, ke);
         Core::mainloop(a, u, smem, acc);
-        if (rem == 0 && end - it == ipt) {
+        if (slot < 0) {
           Core::store(a, u, acc, smem);
-        } else {
-          const int slot = 2 * pid + (it == first_it ? 0 : 1);
-          if (arrive(a, u, slot, acc, flag)) {
-            const int t0 = t * ipt;
-            const int plo = sk_owner(a, t0), phi = sk_owner(a, t0 + ipt - 1);
-            reduce(a, phi - plo + 1, [&](int i) { return 2 * (plo + i) + (sk_start(a, plo + i) >= t0 ? 0 : 1); }, acc);
-            Core::store(a, u, acc, smem);
-            finish_counter(a, u);
-          }
+        } else if (arrive(a, u, slot, acc, flag)) {
+          const int w0 = (t - sk.dp_tiles) * sk.iters;
+          reduce(a, sk.pieces(w0), [&](int i) { return sk.piece_slot(w0, i); }, acc);
+          Core::store(a, u, acc, smem);
+          finish_counter(a, u);
         }
-        it = end;
-      }
-      const int total = a.tiles_m * a.tiles_n;
-      for (int r = 0; r < a.dp_rounds; ++r) {
-        const int t = pid + a.sk_tiles + r * a.programs;
-        if (t >= total) break;
-        Acc acc;
-        Unit u = make_unit(a, t, 0, ipt);
-        Core::mainloop(a, u, smem, acc);
-        Core::store(a, u, acc, smem);
       }
     }
   }

@@ -403,7 +403,13 @@ struct Tile {
         cur = nxt;
       }
     }
-    __syncthreads();  // the ring is reused by the next unit
+    // The last k-steps issued loads for k-tiles past the unit (out-of-range
+    // offsets, which still write zeros into the ring). The compiler does not
+    // count these inline-assembly loads, so __syncthreads() alone would not
+    // wait for them: wait explicitly before the ring is reused (staged
+    // epilogue, next unit's prologue).
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 
   // Plain epilogue D = alpha * acc in a 16-bit type (no C, no fused steps):

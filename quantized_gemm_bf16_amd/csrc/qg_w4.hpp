@@ -51,14 +51,33 @@ struct W4Cfg {
   static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// (x & 0x000F000F) | c for a c whose bits under the mask are zero: the two
-// nibbles at bits 0 and 16 of x become the low mantissa bits of two bf16
-// halves (v_bfi_b32 = (mask & x) | (~mask & c); the mask goes in an SGPR and c
-// in a VGPR, within gfx9's limit of one scalar operand per VALU instruction).
-__device__ __forceinline__ uint32_t nib_bf16(uint32_t x, uint32_t c) {
-  uint32_t d;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(0x000F000Fu), "v"(x), "v"(c));
-  return d;
+// (x & mask) | c with mask = 0x000F000F and a c whose bits under the mask are
+// zero: the two nibbles at bits 0 and 16 of x become the low mantissa bits of
+// two bf16 halves. Written as plain code, not inline assembly: the result
+// feeds an MFMA operand, and the compiler inserts the wait states between a
+// VALU write and an MFMA read of the same register only for instructions it
+// can see (an inline-assembly VALU write followed closely by the MFMA read
+// gave stale operands). The mask comes from opaque_sgpr and c from
+// opaque_vgpr, so that the compiler keeps them in registers and emits one
+// v_and_or_b32 per dword (with both known it folds them into an and and an
+// or with literal operands; with both in scalar registers gfx9's one scalar
+// operand per instruction splits it the same way).
+__device__ __forceinline__ uint32_t nib_bf16(uint32_t x, uint32_t mask, uint32_t c) { return (x & mask) | c; }
+
+// Registers holding V that the compiler cannot constant-fold. Their only
+// consumers are plain VALU instructions (no MFMA reads them), so writing
+// them from inline assembly needs no wait states.
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_sgpr() {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+  return r;
+}
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_vgpr() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
+  return r;
 }
 
 template <class Cfg>
@@ -122,9 +141,8 @@ struct W4 {
     };
 
     const int orow = l & 15, og = l >> 4;
-    // bf16 128.0 in both halves, kept in a VGPR for the bitfield insert
-    uint32_t c128;
-    asm("v_mov_b32 %0, 0x43004300" : "=v"(c128));
+    // bf16 128.0 in both halves, and the nibble mask
+    const uint32_t c128 = opaque_vgpr<0x43004300u>(), m4 = opaque_sgpr<0x000F000Fu>();
     const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};  // bf16 1.0 pairs
     const float zoff = 128.0f + (float)a.zero_point;
 
@@ -168,8 +186,8 @@ struct W4 {
           const uint32_t q = (uint32_t)bw[tn][j];
           // bf16 pairs (128 + q_i, 128 + q_{i+4}) for i = 0..3: one bitfield
           // insert per dword
-          const i32x4 bq = {(int)nib_bf16(q, c128), (int)nib_bf16(q >> 4, c128), (int)nib_bf16(q >> 8, c128),
-                            (int)nib_bf16(q >> 12, c128)};
+          const i32x4 bq = {(int)nib_bf16(q, m4, c128), (int)nib_bf16(q >> 4, m4, c128),
+                            (int)nib_bf16(q >> 8, m4, c128), (int)nib_bf16(q >> 12, m4, c128)};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) P[tn][mt] = mfma16_bf16(bq, af[mt], j == 0 ? f32x4{} : P[tn][mt]);
         }

@@ -149,6 +149,10 @@ class Run:
         return st
 
     def run(self, op=None, **kw):
+        # poison the partials workspace: a split-K / stream-K fixup that read
+        # a slot before (or without) it being written would pick up NaNs
+        if self.ws is not None:
+            self.ws.partials.fill_(float("nan"))
         st = self.launch(op, **kw)
         if st != qg.OK:
             raise qg.QGemmError(st, "qg_run")

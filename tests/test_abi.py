@@ -11,7 +11,6 @@ import re
 import pytest
 
 import quantized_gemm_bf16_amd as qg
-from oracle import streamk_plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 1 << 20  # aligned, never dereferenced
@@ -130,9 +129,93 @@ def test_plan_streamk_matches_planner(g):
     d = dict(kv.split("=") for kv in g.plan(op, Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
     assert d["schedule"] == "streamk" and d["programs"] == "256" and d["grid"] == "256"
     bm, bn, bk = int(d["bm"]), int(d["bn"]), int(d["bk"])
-    pl = streamk_plan(M, N, K, bm, bn, bk, 256)
-    assert int(d["tiles"]) == pl["total_tiles"]
+    assert int(d["tiles"]) == -(-M // bm) * -(-N // bn)
     assert int(d["partials"]) == 2 * 256 * bm * bn * 4
+    assert int(d["barriers"]) == int(d["tiles"]) * 4
+
+
+# ---------------------------------------------------------------- stream-K division
+# (tiles, iters, programs): fewer tiles than programs, a multiple of the
+# program count, ragged waves, one iteration per tile, more programs than
+# iterations, and the decode / 4096^3 shapes
+SK_SHAPES = [(32, 112, 256), (512, 16, 256), (300, 7, 256), (100, 9, 7), (1, 1, 256), (13, 1, 5),
+             (3, 2, 8), (25, 64, 13), (256, 64, 256), (1024, 64, 256), (37, 11, 37), (1000, 3, 64)]
+
+
+@pytest.mark.parametrize("shape", SK_SHAPES)
+def test_streamk_covers_every_iteration_once(shape):
+    T, I, P = shape
+    units = qg.streamk_units(T, I, P)
+    seen = {}
+    for (p, t, kb, ke, slot) in units:
+        assert 0 <= p < P and 0 <= t < T and 0 <= kb < ke <= I
+        for k in range(kb, ke):
+            assert (t, k) not in seen, f"iteration {(t, k)} owned twice"
+            seen[(t, k)] = p
+    assert len(seen) == T * I
+
+
+@pytest.mark.parametrize("shape", SK_SHAPES)
+def test_streamk_balance_and_slots(shape):
+    T, I, P = shape
+    units = qg.streamk_units(T, I, P)
+    per_prog = {}
+    whole = {}
+    slots = set()
+    for (p, t, kb, ke, slot) in units:
+        per_prog[p] = per_prog.get(p, 0) + (ke - kb)
+        if slot < 0:
+            assert kb == 0 and ke == I
+            whole[p] = whole.get(p, 0) + 1
+        else:
+            assert not (kb == 0 and ke == I), "a whole tile must be stored directly"
+            assert slot in (2 * p, 2 * p + 1) and slot not in slots
+            slots.add(slot)
+    work = [per_prog.get(p, 0) for p in range(P)]
+    # every program gets the same whole-tile count before the shared region and
+    # a balanced share of it, so total work differs by at most one iteration
+    assert max(work) - min(work) <= 1
+    if T % P == 0:
+        assert all(s < 0 for (*_, s) in units)
+    # each program's units come out in execution order: whole tiles, then its
+    # shared range in increasing iteration order
+    for p in range(P):
+        mine = [(t, kb, ke) for (q, t, kb, ke, _) in units if q == p]
+        flat = [t * I + kb for (t, kb, ke) in mine]
+        assert flat == sorted(flat)
+
+
+@pytest.mark.parametrize("shape", SK_SHAPES)
+def test_streamk_fixup_order_matches_pieces(shape):
+    # the completing workgroup sums a shared tile's pieces in k order; the
+    # slots it reads must be exactly the slots its pieces were written to
+    T, I, P = shape
+    units = qg.streamk_units(T, I, P)
+    pieces = {}
+    for (p, t, kb, ke, slot) in units:
+        if slot >= 0:
+            pieces.setdefault(t, []).append((kb, ke, slot))
+    for t, lst in pieces.items():
+        lst.sort()
+        assert lst[0][0] == 0 and lst[-1][1] == I
+        assert all(a[1] == b[0] for a, b in zip(lst, lst[1:]))
+        assert qg.streamk_fixup(T, I, P, t) == [s for (_, _, s) in lst]
+
+
+def test_streamk_decode_shape_all_shared():
+    # 32 tiles of 112 iterations over 256 programs: 14 iterations each, every
+    # tile shared by 8 programs
+    units = qg.streamk_units(32, 112, 256)
+    assert len(units) == 256 and all(ke - kb == 14 and s >= 0 for (_, _, kb, ke, s) in units)
+    assert all(len(qg.streamk_fixup(32, 112, 256, t)) == 8 for t in range(32))
+
+
+def test_streamk_units_argument_checks():
+    n = ctypes.c_int()
+    assert qg.lib.qg_streamk_units(4, 0, 2, None, 0, ctypes.byref(n)) == qg.ERR_INVALID_ARG
+    assert qg.lib.qg_streamk_units(4, 3, 2, None, 0, None) == qg.ERR_INVALID_ARG
+    assert qg.lib.qg_streamk_units(4, 3, 3, None, 0, ctypes.byref(n)) == qg.ERR_BUFFER_SMALL and n.value > 0
+    assert qg.lib.qg_streamk_fixup(4, 3, 3, 4, None, 0, ctypes.byref(n)) == qg.ERR_INVALID_ARG
 
 
 def test_plan_square_uses_one_wave_of_big_tiles(g):

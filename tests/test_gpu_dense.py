@@ -1,13 +1,13 @@
 """GPU parity of the dense paths (bf16 / fp16 / int8) against the fp64 oracle,
 called through the C ABI. Sizes span several tiles with ragged tails; the
-full-size workloads are checked on sampled rows."""
+full-size dense workloads are checked on every output."""
 import numpy as np
 import pytest
 import torch
 
 import quantized_gemm_bf16_amd as qg
 import synth
-from tests.gpu_util import Run, check_against_oracle, sample_rows
+from tests.gpu_util import Run, check_against_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -130,14 +130,16 @@ def test_decode_config_full_size(g, ws, M, sched):
     assert int(ws.barriers.abs().sum().item()) == 0
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_square_4096_sampled_rows(g, ws, dtype):
+def test_square_4096_every_output(g, ws, dtype):
+    # the headline configuration as the benchmark runs it (DEFAULT plan), all
+    # 16.8 M outputs against the oracle (about 137 GFLOP of fp64 on the host)
     p = synth.config_square(dtype)
     r = Run(g, p, ws)
     print(r.plan(), flush=True)
     D = r.run()
-    rows = sample_rows(4096, 24)
-    check_against_oracle(p, D, rows=rows, what=f"4096^3 {dtype}")
+    check_against_oracle(p, D, what=f"4096^3 {dtype}")
 
 
 # ---------------------------------------------------------------- int8 -> int32, bit-exact
@@ -160,10 +162,11 @@ def test_int8_decode_split8_exact(g, ws):
     check_against_oracle(p, r.run(op), what="int8 decode stream-K")
 
 
-def test_int8_square_4096_sampled(g, ws):
+@pytest.mark.timeout(300)
+def test_int8_square_4096_every_output(g, ws):
     p = synth.dense_problem(4096, 4096, 4096, "i8", "i32", seed=3)
     D = Run(g, p, ws).run()
-    check_against_oracle(p, D, rows=sample_rows(4096, 8), what="int8 4096^3")
+    check_against_oracle(p, D, what="int8 4096^3")
 
 
 # ---------------------------------------------------------------- grouped
@@ -232,7 +235,7 @@ def test_skinny_shared_a_ring_matches_per_wave_a(g, ws, dt):
         print(kn, r.plan(op), flush=True)
         out[kn] = r.run(op)
     a, b = out.values()
-    check_against_oracle(p, a, rows=sample_rows(16, 4), what=f"shared-A decode {dt}")
+    check_against_oracle(p, a, what=f"shared-A decode {dt}")
     assert np.array_equal(a, b)
     assert int(ws.barriers.abs().sum().item()) == 0
 

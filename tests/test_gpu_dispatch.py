@@ -66,18 +66,47 @@ def test_measure_refuses_aliased_c_and_d():
     ws = qg.workspace()
     g = qg.Gemm()
     M, N, K = 16, 256, 512
-    A = torch.randn(M, K, device="cuda").to(torch.bfloat16)
-    B = torch.randn(N, K, device="cuda").to(torch.bfloat16)
-    CD = torch.randn(M, N, device="cuda").to(torch.bfloat16)
-    L = qg.layout
-    st = g.run_raw(qg.operation(policy=qg.POLICY_MEASURE), 1.0, A, L("bf16", M, K), None, None, B, L("bf16", N, K),
-                   None, None, 1.0, CD, L("bf16", M, N), CD, L("bf16", M, N), ws.desc)
+    p = synth.dense_problem(M, N, K, "bf16", "bf16", c_dtype="bf16", alpha=1.0, beta=1.0,
+                            a_std=0.02, b_std=0.02, seed=12)
+    r = Run(g, p, ws)
+    CD = r.C.clone()  # D aliases C: D = A @ B + D
+    Cd = qg.layout("bf16", M, N, ld=r.ldn)
+    st = g.run_raw(qg.operation(policy=qg.POLICY_MEASURE), 1.0, r.A, r.Ad, None, None, r.B, r.Bd,
+                   None, None, 1.0, CD, Cd, CD, Cd, ws.desc)
     assert st == qg.ERR_UNSUPPORTED
-    # DEFAULT accepts the in-place update D = A @ B + D
-    ref = (A.float() @ B.float().T + CD.float())
-    st = g.run_raw(qg.operation(), 1.0, A, L("bf16", M, K), None, None, B, L("bf16", N, K),
-                   None, None, 1.0, CD, L("bf16", M, N), CD, L("bf16", M, N), ws.desc)
+    torch.cuda.synchronize()
+    assert torch.equal(CD, r.C), "a refused call must not have touched D"
+    # DEFAULT accepts the in-place update; every output against the oracle
+    st = g.run_raw(qg.operation(), 1.0, r.A, r.Ad, None, None, r.B, r.Bd, None, None, 1.0, CD, Cd, CD, Cd, ws.desc)
     assert st == qg.OK
     torch.cuda.synchronize()
-    # bf16 output: one rounding of |ref| (2^-8 relative) plus the fp32 sum
-    assert torch.allclose(CD.float(), ref, rtol=2 ** -7, atol=1e-2)
+    D = CD.view(torch.bfloat16).double().cpu().numpy()[:, :N]  # C was uploaded as bf16 bit patterns
+    check_against_oracle(p, D, what="in-place D = A @ B + D")
+
+
+def test_measure_policy_under_graph_capture_does_not_measure():
+    # measuring synchronises the stream; under capture the engine resolves
+    # like DEFAULT instead and leaves the cache empty
+    ws = qg.workspace()
+    g = qg.Gemm()
+    p = synth.dense_problem(16, 1024, 2048, "bf16", "bf16", c_dtype="bf16", alpha=1.0, beta=1.0,
+                            a_std=0.02, b_std=0.02, seed=6)
+    r = Run(g, p, ws)
+    op = r.op(policy=qg.POLICY_MEASURE)
+    eager_default = r.run(r.op())
+    ws.partials.fill_(float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert r.launch(op) == qg.OK
+    assert g.cache_size() == 0
+    for rep in range(3):
+        r.D.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = r.D.double().cpu().numpy()[:, :p["N"]]
+        assert np.array_equal(got, eager_default), f"replay {rep}"
+    check_against_oracle(p, eager_default, what="MEASURE under capture")
+    # outside capture the same call measures and fills the cache
+    r.run(op)
+    assert g.cache_size() == 1

@@ -355,30 +355,6 @@ def test_row_sampling_matches_full():
     assert np.array_equal(part, full[rows]) and np.array_equal(pa, fa[rows])
 
 
-# ---------------------------------------------------------------- stream-K plan
-def test_streamk_plan_hand_evaluated_example():
-    with open(os.path.join(GOLDEN, "streamk_plan_tutorial_call.json")) as f:
-        g = json.load(f)
-    got = oracle.streamk_plan(*g["args"])
-    assert got == g["plan"]
-    segs = oracle.streamk_segments(*g["args"])
-    assert sum(e - b for (_, _, b, e) in segs) == g["plan"]["total_tiles"] * g["plan"]["iters_per_tile"]
-
-
-@pytest.mark.parametrize("shape", [(256, 1024, 512, 16, 128, 32, 108), (16, 4096, 14336, 16, 64, 128, 256),
-                                   (4096, 4096, 4096, 256, 256, 64, 256), (100, 300, 70, 32, 64, 16, 7),
-                                   (1, 1, 1, 16, 16, 16, 256), (640, 640, 1000, 128, 128, 64, 13)])
-def test_streamk_covers_each_iteration_once(shape):
-    pl = oracle.streamk_plan(*shape)
-    seen = {}
-    for (pid, tile, b, e) in oracle.streamk_segments(*shape):
-        assert 0 <= tile < pl["total_tiles"] and 0 <= b < e <= pl["iters_per_tile"]
-        for it in range(b, e):
-            assert (tile, it) not in seen
-            seen[(tile, it)] = pid
-    assert len(seen) == pl["total_tiles"] * pl["iters_per_tile"]
-
-
 # ---------------------------------------------------------------- generator
 def test_zipf_counts_properties():
     c = synth.zipf_counts()
