@@ -234,6 +234,33 @@ int qg_run(qg_handle* h, const qg_operation* op, float alpha,
            void* D, const qg_layout* Ddesc,
            const qg_workspace* ws, hipStream_t stream);
 
+/* qg_run without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The split-K / stream-K workspace is a device array
+ * inside the library, one per GPU, held until the process ends:
+ * qg_noalloc_barriers_size() bytes of arrival counters (64 KiB: 16384 split
+ * tiles) and qg_noalloc_partials_size() bytes of partial tiles (16 MiB). The
+ * first call on a device looks the array up and clears its counters on
+ * `stream`; every run leaves them zero again. Arguments, plans and kernels
+ * are those of qg_run (the heuristic sees the smaller workspace, so it may
+ * pick a smaller split); a plan that needs more workspace than the array
+ * holds returns QG_ERR_WORKSPACE, and QG_POLICY_MEASURE returns
+ * QG_ERR_UNSUPPORTED (measuring creates events and synchronises). No device
+ * memory is allocated or freed. All calls on one GPU share its array: calls
+ * whose kernels may overlap on that GPU (other streams, other threads) race
+ * and must be serialised by the caller. */
+int qg_run_noalloc(qg_handle* h, const qg_operation* op, float alpha,
+                   const void* A, const qg_layout* Adesc,
+                   const void* U, const qg_layout* Udesc,
+                   const void* B, const qg_layout* Bdesc,
+                   const void* V, const qg_layout* Vdesc,
+                   float beta,
+                   const void* C, const qg_layout* Cdesc,
+                   void* D, const qg_layout* Ddesc,
+                   hipStream_t stream);
+size_t qg_noalloc_barriers_size(void);
+size_t qg_noalloc_partials_size(void);
+
 /* What qg_run would launch for these arguments, without launching (no
  * device access, no measuring). `desc` receives a NUL-terminated text line
  * "kernel=<name> schedule=<dp|splitk|streamk|grouped> split=<s> programs=<p>

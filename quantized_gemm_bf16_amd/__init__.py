@@ -32,7 +32,8 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3, "i8": I8, "i3
 
 EXPORTS = ["qg_create", "qg_destroy", "qg_barriers_size", "qg_partials_size", "qg_run", "qg_plan",
            "qg_export", "qg_import", "qg_get_tuning_seq", "qg_cache_size", "qg_kernel_count",
-           "qg_kernel_name", "qg_status_str", "qg_version", "qg_streamk_units", "qg_streamk_fixup"]
+           "qg_kernel_name", "qg_status_str", "qg_version", "qg_streamk_units", "qg_streamk_fixup",
+           "qg_run_noalloc", "qg_noalloc_barriers_size", "qg_noalloc_partials_size"]
 
 
 class Layout(ctypes.Structure):
@@ -85,6 +86,10 @@ def _load(path=LIB_PATH):
     L.qg_partials_size.restype = sz
     L.qg_run.argtypes = [vp, P(Operation), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp, P(Layout), vp,
                          P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout), P(Workspace), vp]
+    L.qg_run_noalloc.argtypes = [vp, P(Operation), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp, P(Layout),
+                                 vp, P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp]
+    L.qg_noalloc_barriers_size.restype = sz
+    L.qg_noalloc_partials_size.restype = sz
     L.qg_plan.argtypes = [vp, P(Operation), P(Layout), P(Layout), P(Layout), P(Layout), P(Layout), P(Layout),
                           ctypes.c_float, ctypes.c_float, P(Workspace), ctypes.c_char_p, sz]
     L.qg_export.argtypes = [vp, ctypes.c_char_p, sz, P(sz)]
@@ -99,7 +104,7 @@ def _load(path=LIB_PATH):
     L.qg_version.restype = ctypes.c_char_p
     L.qg_streamk_units.argtypes = [i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
     L.qg_streamk_fixup.argtypes = [i32, i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
-    for name in ("qg_create", "qg_destroy", "qg_run", "qg_plan", "qg_export", "qg_import",
+    for name in ("qg_create", "qg_destroy", "qg_run", "qg_run_noalloc", "qg_plan", "qg_export", "qg_import",
                  "qg_get_tuning_seq", "qg_cache_size", "qg_streamk_units", "qg_streamk_fixup"):
         getattr(L, name).restype = i32
     return L
@@ -122,6 +127,14 @@ def barriers_size() -> int:
 
 def partials_size() -> int:
     return int(lib.qg_partials_size())
+
+
+def noalloc_barriers_size() -> int:
+    return int(lib.qg_noalloc_barriers_size())
+
+
+def noalloc_partials_size() -> int:
+    return int(lib.qg_noalloc_partials_size())
 
 
 def kernel_names():
@@ -209,6 +222,13 @@ class Gemm:
     def run(self, *args, **kw):
         _check(self.run_raw(*args, **kw), "qg_run")
 
+    def run_noalloc_raw(self, op, alpha, A, Ad, U, Ud, B, Bd, V, Vd, beta, C, Cd, D, Dd, stream=None) -> int:
+        """qg_run_noalloc (workspace from the library's own device array); returns the status code."""
+        def r(x):
+            return None if x is None else ctypes.byref(x)
+        return lib.qg_run_noalloc(self.h, ctypes.byref(op), float(alpha), _ptr(A), r(Ad), _ptr(U), r(Ud), _ptr(B),
+                                  r(Bd), _ptr(V), r(Vd), float(beta), _ptr(C), r(Cd), _ptr(D), r(Dd),
+                                  stream if stream is not None else _current_stream())
 
     def plan(self, op, Ad, Ud, Bd, Vd, Cd, Dd, alpha, beta, ws=None) -> str:
         buf = ctypes.create_string_buffer(512)
