@@ -556,9 +556,9 @@ Choice heuristic(const qg_handle* h, const Problem& p, const qg_workspace* ws, i
   }
   const bool ws_ok = ws && ws->partials && ws->barriers;
   if (p.tb == QG_U4) {
-    // 32-row tiles up to M = 64: twice the tiles, so half the split factor
-    // (and half the partial-tile traffic) for the same number of workgroups
-    c.kernel = kernel_by_shape(p, p.M <= 64 ? 32 : 64, 256);
+    // the smallest row tile that covers M (16, 32, then 64-row tiles), so B
+    // is read once per 64 rows
+    c.kernel = kernel_by_shape(p, p.M <= 16 ? 16 : (p.M <= 32 ? 32 : 64), 128);
     if (c.kernel < 0) return c;
     const KernelInfo& k = kKernels[c.kernel];
     const int64_t tiles = cdiv(p.M, k.bm) * cdiv(p.N, k.bn), iters = cdiv(p.K, k.bk);

@@ -13,7 +13,7 @@ namespace qg {
 #undef QG_TILE_BF16_BIG
 #define QG_TILE_BF16_BIG(BM, BN, WM, WN, ST, RB) \
   template hipError_t launch_tile<TileCfg<El::BF16, BM, BN, WM, WN, ST, RB>>(const Args&, int, hipStream_t);
-#define QG_W4(BM, BN, NW, ST)
+#define QG_W4(MT, BN, WN, WK, ST)
 #define QG_F8(BM, BN, WM, WN, ST)
 #include "qg_kernel_list.inc"
 }  // namespace qg

@@ -12,7 +12,7 @@ namespace qg {
 #undef QG_SKINNY_BF16
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) \
   template hipError_t launch_skinny<SkinnyCfg<El::BF16, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
-#define QG_W4(BM, BN, NW, ST)
+#define QG_W4(MT, BN, WN, WK, ST)
 #define QG_F8(BM, BN, WM, WN, ST)
 #include "qg_kernel_list.inc"
 }  // namespace qg

@@ -10,7 +10,7 @@ namespace qg {
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS)
-#define QG_W4(BM, BN, NW, ST)
+#define QG_W4(MT, BN, WN, WK, ST)
 #define QG_F8(BM, BN, WM, WN, ST) \
   template hipError_t launch_f8<F8Cfg<BM, BN, WM, WN, ST>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"

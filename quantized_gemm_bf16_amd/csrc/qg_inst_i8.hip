@@ -15,7 +15,7 @@ namespace qg {
   template hipError_t launch_tile<TileCfg<El::I8, BM, BN, WM, WN, ST, RB>>(const Args&, int, hipStream_t);
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) \
   template hipError_t launch_skinny<SkinnyCfg<El::I8, BN, NW, MT, DP, BB, NS>>(const Args&, int, hipStream_t);
-#define QG_W4(BM, BN, NW, ST)
+#define QG_W4(MT, BN, WN, WK, ST)
 #define QG_F8(BM, BN, WM, WN, ST)
 #include "qg_kernel_list.inc"
 }  // namespace qg

@@ -9,7 +9,8 @@ namespace qg {
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS)
-#define QG_W4(BM, BN, NW, ST) template hipError_t launch_w4<W4Cfg<BM, BN, NW, ST>>(const Args&, int, hipStream_t);
+#define QG_W4(MT, BN, WN, WK, ST) \
+  template hipError_t launch_w4<W4Cfg<MT, BN, WN, WK, ST>>(const Args&, int, hipStream_t);
 #define QG_F8(BM, BN, WM, WN, ST)
 #include "qg_kernel_list.inc"
 }  // namespace qg

@@ -17,8 +17,8 @@ namespace qg {
 #define QG_SKINNY_BF16(BN, NW, MT, DP, BB, NS) QG_DECL_SK(BF16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS) QG_DECL_SK(F16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) QG_DECL_SK(I8, BN, NW, MT, DP, BB, NS)
-#define QG_W4(BM, BN, NW, ST) \
-  extern template hipError_t launch_w4<W4Cfg<BM, BN, NW, ST>>(const Args&, int, hipStream_t);
+#define QG_W4(MT, BN, WN, WK, ST) \
+  extern template hipError_t launch_w4<W4Cfg<MT, BN, WN, WK, ST>>(const Args&, int, hipStream_t);
 #define QG_F8(BM, BN, WM, WN, ST) \
   extern template hipError_t launch_f8<F8Cfg<BM, BN, WM, WN, ST>>(const Args&, int, hipStream_t);
 #include "qg_kernel_list.inc"
@@ -48,9 +48,10 @@ namespace qg {
 #define QG_SKINNY_F16(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(F16, DT_F16, BN, NW, MT, DP, BB, NS)
 #define QG_SKINNY_I8(BN, NW, MT, DP, BB, NS) QG_ENTRY_SK(I8, DT_I8, BN, NW, MT, DP, BB, NS)
 
-#define QG_W4(BM, BN, NW, ST)                                                                          \
-  {"w4_BF16_" #BM "x" #BN "_w" #NW "_s" #ST, FAM_W4, DT_BF16, BM, BN, 128, ST, NW * 64, BM * BN * 4, \
-   &launch_w4<W4Cfg<BM, BN, NW, ST>>},
+#define QG_W4(MT, BN, WN, WK, ST)                                                                     \
+  {"w4_BF16_" #MT "x16x" #BN "_w" #WN "x" #WK "_s" #ST, FAM_W4, DT_BF16, 16 * MT, BN,                     \
+   W4Cfg<MT, BN, WN, WK, ST>::BK, ST, W4Cfg<MT, BN, WN, WK, ST>::NT, 16 * MT * BN * 4,                   \
+   &launch_w4<W4Cfg<MT, BN, WN, WK, ST>>},
 
 #define QG_F8(BM, BN, WM, WN, ST)                                                                         \
   {"f8_E4M3_" #BM "x" #BN "_w" #WM "x" #WN "_s" #ST, FAM_F8, DT_E4M3, BM, BN, 128, ST, WM * WN * 64, BM * BN * 4, \

@@ -9,21 +9,30 @@
 // Lmdeploy Gemm MainloopSm80V2": the scale advances once per group along K).
 //
 // Dequantisation in registers, before the MFMA, without rounding the weight:
-// a nibble q becomes the bf16 number 128 + q with one bitfield insert (bf16 0x4300 is
-// 128 and its last mantissa bit weighs 1), two nibbles per dword. Per group
-// the MFMA computes P = sum_k a_k (128 + q_k); a second MFMA against a column
-// of ones gives R = sum_k a_k; the group then adds
-//     s_n * (P - (128 + zp) * R)
-// to the fp32 accumulator. Both MFMA products are exact and accumulate in
-// fp32, so the only rounding is fp32 summation.
+// a nibble q becomes the bf16 number 128 + q (bf16 0x4300 is 128 and its last
+// mantissa bit weighs 1). Per group the MFMA chain computes
+//     P = sum_k a_k (128 + q_k)      and      Z = sum_k a_k (128 + zp)
+// with the same A fragments in the same order (Z from a B operand holding
+// the constant 128 + zp), and the group adds s_n * (P - Z) to the fp32
+// accumulator. Both products are exact; the only rounding is the fp32
+// summation, and a column whose nibbles all equal the zero point in a group
+// gives P == Z bit for bit, so it contributes exactly 0.
 //
-// Tile: BM x BN outputs, one 128-deep k group per k-tile. A k-tile (BM rows x
-// 256 bytes), the B k-tile (BN rows x 64 bytes of nibbles) and the k-tile's
-// scales (BN dwords) go global -> LDS with direct loads into an S-stage ring
-// shared by the NW waves (wave w owns columns [w*BN/NW, (w+1)*BN/NW)). The
-// 128 k of a group map to MFMA k-slots as: step j, lane group g (lanes
-// 16g..16g+15) takes k 32g + 8j + {0,4,1,5,2,6,3,7}; A fragments are
-// byte-permuted into that order (v_perm), B comes out of the bitfield insert in it.
+// Nibble order: a word w of 8 nibbles (k0 .. k0+7) and y = w >> 4 are merged
+// by one byte permute per dword into [byte r of w, -, byte r of y, -], whose
+// two low nibbles under the mask 0x000F000F are q(k0 + 2r) and q(k0 + 2r + 1):
+// OR-ed with 0x43004300 they are the bf16 pair (128 + q(k0+2r), 128 +
+// q(k0+2r+1)), i.e. B comes out in natural k order and the A fragments are
+// used exactly as they sit in LDS.
+//
+// Tile: BM x BN outputs (BM = 16 MT). 8 waves as WN column groups x WK
+// k-groups: wave (wn, wk) owns columns [wn BNW, (wn+1) BNW) and, of each
+// k-tile of WK scale groups (128 WK deep), group wk. A k-tile's A rows (BM x
+// 256 WK bytes), B rows (BN x 64 WK bytes of nibbles), the scales (one dword
+// per column: WK = 2 fp16) and the zero points (one dword per column) go
+// global -> LDS with direct loads into an S-stage ring. At the end of a unit
+// the WK partial sums are added through LDS in wk order (deterministic), and
+// the wk = 0 waves hold the tile.
 #pragma once
 #include <type_traits>
 
@@ -31,42 +40,48 @@
 
 namespace qg {
 
-template <int BM_, int BN_, int NW_, int STAGES_>
+template <int MT_, int BN_, int WN_, int WK_, int STAGES_>
 struct W4Cfg {
-  static constexpr int BM = BM_, BN = BN_, NW = NW_, STAGES = STAGES_;
-  static constexpr int NT = NW * 64, MT = BM / 16, BNW = BN / NW, TN = BNW / 16;
-  static constexpr int BK = 128;                  // k per k-tile (= one scale group)
-  static constexpr int A_ROWB = 256, B_ROWB = 64;  // bytes per row per k-tile
-  // scales: every lane of a dword load writes LDS, so each wave gets 64 dword
-  // slots; lanes past its BN/NW columns load nothing (zeros).
-  static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB, S_BYTES = NW * 64 * 4;
-  static constexpr int Z_BYTES = NW * 64 * 4;  // per-group zero points (a dword per lane)
+  static constexpr int MT = MT_, BM = 16 * MT_, BN = BN_, WN = WN_, WK = WK_, STAGES = STAGES_;
+  static constexpr int NW = WN * WK, NT = NW * 64, BNW = BN / WN, TN = BNW / 16;
+  static constexpr int GK = 128;                    // scale group
+  static constexpr int BK = GK * WK;                // k per k-tile
+  static constexpr int A_ROWB = BK * 2, B_ROWB = BK / 2;
+  static constexpr int A_CPR = A_ROWB / 16, A_RPI = 64 / A_CPR;  // 16-byte chunks per row, rows per 64-lane load
+  static constexpr int B_CPR = B_ROWB / 16, B_RPI = 64 / B_CPR;
+  static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB;
+  static constexpr int S_BYTES = BN * 4, Z_BYTES = BN * 4;  // one dword per column each
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + Z_BYTES;
-  static constexpr int LA = BM / 4 / NW;   // 64-lane A loads per wave (4 rows x 256 B each)
-  static constexpr int LB = BN / 16 / NW;  // 64-lane B loads per wave (16 rows x 64 B each)
-  static constexpr int LPW = LA + LB + 2;  // + one scale load and one zero-point load (dword each)
-  static_assert(LA * 4 * NW == BM && LB * 16 * NW == BN, "rows must split over waves");
-  static_assert(BNW % 16 == 0 && BNW <= 64, "columns per wave");
-  static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024 - 4096, "LDS budget");
+  static constexpr int DUMMY = STAGES * STAGE;              // 256 bytes the spare dword loads write
+  static constexpr int ZX = DUMMY + 256;                    // Z exchange: [2][WK][4][16][MT] floats
+  static constexpr int SMEM = ZX + 2 * WK * 4 * 16 * MT * 4;
+  static constexpr int LA = BM / A_RPI / NW;  // 64-lane A loads per wave per k-tile
+  static constexpr int LB = BN / B_RPI / NW;  // 64-lane B loads per wave per k-tile
+  static constexpr int SW = BN / 64;          // waves loading scales (and as many loading zero points)
+  static constexpr int LPW = LA + LB + 1;     // + one dword load (scales, zero points or a spare)
+  static_assert(WK == 2, "a scale dword holds the k-tile's two fp16 scales");
+  static_assert(A_RPI >= 1 && LA * A_RPI * NW == BM, "A rows must split over waves");
+  static_assert(LB * B_RPI * NW == BN, "B rows must split over waves");
+  static_assert(BN % 64 == 0 && 2 * SW <= NW, "scale and zero-point loaders");
+  static_assert(TN >= 1 && BNW % 16 == 0, "columns per wave");
+  static_assert(MT <= WN, "one wave per m-tile computes the shared Z chain");
+  static_assert(STAGES >= 2 && SMEM <= 160 * 1024 - 8192, "LDS budget");
   static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(WN * TN * MT * 64 * 16 * (WK - 1) <= SMEM, "space for the k-group sum");
 };
 
 // (x & mask) | c with mask = 0x000F000F and a c whose bits under the mask are
-// zero: the two nibbles at bits 0 and 16 of x become the low mantissa bits of
-// two bf16 halves. Written as plain code, not inline assembly: the result
-// feeds an MFMA operand, and the compiler inserts the wait states between a
-// VALU write and an MFMA read of the same register only for instructions it
-// can see (an inline-assembly VALU write followed closely by the MFMA read
-// gave stale operands). The mask comes from opaque_sgpr and c from
-// opaque_vgpr, so that the compiler keeps them in registers and emits one
-// v_and_or_b32 per dword (with both known it folds them into an and and an
-// or with literal operands; with both in scalar registers gfx9's one scalar
-// operand per instruction splits it the same way).
+// zero. Written as plain code, not inline assembly: the result feeds an MFMA
+// operand, and the compiler inserts the wait states between a VALU write and
+// an MFMA read of the same register only for instructions it can see (an
+// inline-assembly VALU write followed closely by the MFMA read gave stale
+// operands). The mask comes from opaque_sgpr and c from opaque_vgpr, so that
+// the compiler keeps them in registers and emits one v_and_or_b32 per dword.
 __device__ __forceinline__ uint32_t nib_bf16(uint32_t x, uint32_t mask, uint32_t c) { return (x & mask) | c; }
 
 // Registers holding V that the compiler cannot constant-fold. Their only
-// consumers are plain VALU instructions (no MFMA reads them), so writing
-// them from inline assembly needs no wait states.
+// consumers are plain VALU instructions (no MFMA reads them directly), so
+// writing them from inline assembly needs no wait states.
 template <uint32_t V>
 __device__ __forceinline__ uint32_t opaque_sgpr() {
   uint32_t r;
@@ -83,169 +98,322 @@ __device__ __forceinline__ uint32_t opaque_vgpr() {
 template <class Cfg>
 struct W4 {
   static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, TN = Cfg::TN, MT = Cfg::MT;
-  static constexpr int SMEM_BYTES = Cfg::STAGES * Cfg::STAGE;
+  static constexpr int WN = Cfg::WN, WK = Cfg::WK, BNW = Cfg::BNW;
+  static constexpr int SMEM_BYTES = Cfg::SMEM;
   struct Acc {
     f32x4 v[TN][MT];
   };
 
+  __device__ __forceinline__ static int wn_of(int w) { return w % WN; }
+  __device__ __forceinline__ static int wk_of(int w) { return w / WN; }
+
   __device__ __forceinline__ static void mainloop(const Args& a, const Unit& u, char* smem, Acc& acc) {
     const int w = wave_id(), l = lane_id();
+    const int wn = wn_of(w), wk = wk_of(w);
     const int64_t lda_b = a.lda * 2, ldb_b = a.ldb * 4, ldv_b = a.ldv * 2;
-    const uint32_t kbytes_a = (uint32_t)a.K * 2;  // valid bytes of an A row
+    const uint32_t abytes = (uint32_t)a.K * 2, bbytes = (uint32_t)a.K / 2;  // valid bytes of an A / B row
+    const int groups = a.K / Cfg::GK;
     const int a_rows = max(0, min(BM, u.m_end - u.m0));
     const int b_rows = max(0, min(BN, a.N - u.n0));
     const i32x4 rA = make_rsrc_words((const char*)a.A + (int64_t)u.m0 * lda_b, (uint32_t)(a_rows * lda_b));
     const i32x4 rB = make_rsrc_words((const char*)a.B + (int64_t)u.n0 * ldb_b, (uint32_t)(b_rows * ldb_b));
-    const i32x4 rV = make_rsrc_words((const char*)a.V + (int64_t)u.n0 * ldv_b, (uint32_t)(b_rows * ldv_b));
     // per-group zero points (bytes, U[n, group]); without them the loads read nothing
     const bool has_z = a.U != nullptr;
     const int64_t ldz_b = a.ldu;
-    const i32x4 rZ = make_rsrc_words(has_z ? (const char*)a.U + (int64_t)u.n0 * ldz_b : (const char*)a.V,
-                                     has_z ? (uint32_t)(b_rows * ldz_b) : 0u);
+    // waves [0, SW) load scales, [SW, 2 SW) zero points, the rest a spare dword
+    const int role = w < Cfg::SW ? 0 : (w < 2 * Cfg::SW ? 1 : 2);
+    const int dcol = (role == 1 ? w - Cfg::SW : w) * 64 + l;  // column of this lane's dword
+    const i32x4 rD = role == 0 ? make_rsrc_words((const char*)a.V + (int64_t)u.n0 * ldv_b, (uint32_t)(b_rows * ldv_b))
+                               : make_rsrc_words(has_z ? (const char*)a.U + (int64_t)u.n0 * ldz_b : (const char*)a.V,
+                                                 role == 1 && has_z ? (uint32_t)(b_rows * ldz_b) : 0u);
 
     // load addressing (lane -> LDS position fixed; the lane fetches the
     // logical chunk the swizzle stores there)
     uint32_t offA[Cfg::LA], chA[Cfg::LA], offB[Cfg::LB], chB[Cfg::LB];
 #pragma unroll
     for (int i = 0; i < Cfg::LA; ++i) {
-      const int row = (w * Cfg::LA + i) * 4 + (l >> 4);
-      chA[i] = (uint32_t)(((l & 15) ^ (row & 15)) * 16);
+      const int row = (w * Cfg::LA + i) * Cfg::A_RPI + l / Cfg::A_CPR;
+      chA[i] = (uint32_t)(((l % Cfg::A_CPR) ^ (row & 15)) * 16);
       offA[i] = (uint32_t)(row * lda_b) + chA[i];
     }
 #pragma unroll
     for (int i = 0; i < Cfg::LB; ++i) {
-      const int row = (w * Cfg::LB + i) * 16 + (l >> 2);
-      chB[i] = (uint32_t)(((l & 3) ^ ((row >> 2) & 3)) * 16);
+      const int row = (w * Cfg::LB + i) * Cfg::B_RPI + l / Cfg::B_CPR;
+      chB[i] = (uint32_t)(((l % Cfg::B_CPR) ^ ((row >> 1) & 7)) * 16);
       offB[i] = (uint32_t)(row * ldb_b) + chB[i];
     }
-    // scales: wave w loads the dwords holding s(n, group) for its BN/NW rows
-    const int srow = w * Cfg::BNW + l;
-    const bool s_lane = l < Cfg::BNW;
+    char* dptr = role == 0 ? smem + Cfg::A_BYTES + Cfg::B_BYTES + w * 256
+                           : (role == 1 ? smem + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::S_BYTES + (w - Cfg::SW) * 256
+                                        : smem + Cfg::DUMMY);
+    const uint32_t dstride = role == 2 ? 0u : (uint32_t)Cfg::STAGE;
 
     auto issue = [&](int stage, int kt) {
       char* sb = smem + stage * Cfg::STAGE;
       const bool live = kt < u.ke;
       const uint32_t ka = (uint32_t)kt * Cfg::A_ROWB, kb = (uint32_t)kt * Cfg::B_ROWB;
+      if (live && ka + Cfg::A_ROWB <= abytes) {
+        // the whole k-tile lies inside K (the usual case): no per-lane range selects
 #pragma unroll
-      for (int i = 0; i < Cfg::LA; ++i)
-        load_lds_x4(rA, sb + (w * Cfg::LA + i) * 1024, live && ka + chA[i] < kbytes_a ? offA[i] + ka : kOOB);
+        for (int i = 0; i < Cfg::LA; ++i) load_lds_x4(rA, sb + (w * Cfg::LA + i) * 1024, offA[i] + ka);
 #pragma unroll
-      for (int i = 0; i < Cfg::LB; ++i)
-        load_lds_x4(rB, sb + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024, live ? offB[i] + kb : kOOB);
-      // dword (aligned) that holds s(n0 + srow, kt); ldv is even, so the half is kt & 1
-      const uint32_t soff = (uint32_t)(srow * ldv_b) + ((uint32_t)kt * 2 & ~3u);
-      load_lds_x1a(rV, sb + Cfg::A_BYTES + Cfg::B_BYTES + w * 256, live && s_lane ? soff : kOOB);
-      // dword (aligned) that holds z(n0 + srow, kt): byte kt & 3 of it (ldu is a multiple of 4)
-      const uint32_t zo = (uint32_t)(srow * ldz_b) + ((uint32_t)kt & ~3u);
-      load_lds_x1a(rZ, sb + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::S_BYTES + w * 256, live && s_lane && has_z ? zo : kOOB);
+        for (int i = 0; i < Cfg::LB; ++i) load_lds_x4(rB, sb + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024, offB[i] + kb);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::LA; ++i)
+          load_lds_x4(rA, sb + (w * Cfg::LA + i) * 1024, live && ka + chA[i] < abytes ? offA[i] + ka : kOOB);
+#pragma unroll
+        for (int i = 0; i < Cfg::LB; ++i)
+          load_lds_x4(rB, sb + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024,
+                      live && kb + chB[i] < bbytes ? offB[i] + kb : kOOB);
+      }
+      // scales: the dword holding s(n, 2 kt) and s(n, 2 kt + 1); zero points:
+      // the dword holding z(n, 2 kt) (ldu is a multiple of 16)
+      const uint32_t doff = role == 0 ? (uint32_t)(dcol * ldv_b) + (uint32_t)kt * 4
+                                      : (uint32_t)(dcol * ldz_b) + ((uint32_t)(2 * kt) & ~3u);
+      load_lds_x1a(rD, dptr + stage * dstride, live && role < 2 ? doff : kOOB);
     };
 
     const int orow = l & 15, og = l >> 4;
-    // bf16 128.0 in both halves, and the nibble mask
     const uint32_t c128 = opaque_vgpr<0x43004300u>(), m4 = opaque_sgpr<0x000F000Fu>();
-    const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};  // bf16 1.0 pairs
-    const float zoff = 128.0f + (float)a.zero_point;
+    // byte permutes: dword r = [byte r of w, 0, byte r of (w >> 4), 0]
+    constexpr uint32_t kSel0 = 0x0C040C00u, kSel1 = 0x0C050C01u, kSel2 = 0x0C060C02u, kSel3 = 0x0C070C03u;
+    // B operand of the Z chain (symmetric): 128 + zp in every bf16 half
+    const uint32_t zsym = c128 | ((uint32_t)a.zero_point * 0x00010001u);
+    // Symmetric Z exchange: Z depends on the row only, so for each group the
+    // wave with wn = mt computes the chain of m-tile mt and leaves the 16 row
+    // values in zx[group parity][wk][lane group][row][mt]; every wave applies
+    // the group's correction one k-tile later, after the barrier that makes
+    // them visible.
+    float* zx = (float*)(smem + Cfg::ZX);
+    auto zslot = [](int kt, int wk_, int og_) { return (((kt & 1) * WK + wk_) * 4 + og_) * 16 * MT; };
 
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = f32x4{};
 
-    // One k-tile (one scale group) from ring stage st.
-    auto group = [&](int st, int kt) {
+    // P (and, with zero points, Z) of group 2 kt + wk of the k-tile in ring
+    // stage st, plus the group's scales of the lane's columns (0 past K).
+    auto group = [&](int st, int kt, auto with_z, f32x4 (&P)[TN][MT], float (&sc)[TN][4], auto&& hook) {
+      constexpr bool ZP = decltype(with_z)::value;
       const char* sA = smem + st * Cfg::STAGE;
       const char* sB = sA + Cfg::A_BYTES;
       const uint32_t* sS = (const uint32_t*)(sB + Cfg::B_BYTES);
-      // B words of this lane: row orow of each n-tile, 16-byte chunk og (4 words, one per step)
+      const uint32_t* sZ = (const uint32_t*)((const char*)sS + Cfg::S_BYTES);
+      const int g = 2 * kt + wk;
+      // B words of this lane: row orow of each n-tile, the group's 16-byte
+      // chunk og (4 words, one per k-step)
       i32x4 bw[TN];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int row = w * Cfg::BNW + tn * 16 + orow;
-        bw[tn] = *(const i32x4*)(sB + row * Cfg::B_ROWB + ((og ^ ((row >> 2) & 3)) << 4));
+        const int row = wn * BNW + tn * 16 + orow;
+        const int c = wk * 4 + og;
+        bw[tn] = *(const i32x4*)(sB + row * Cfg::B_ROWB + ((c ^ ((row >> 1) & 7)) << 4));
       }
-      f32x4 P[TN][MT], R[MT];
+      // scales of the lane's output columns n = 4 og + r; a group past K (the
+      // second of a k-tile when K / 128 is odd) has P = Z = 0 and its scale
+      // slot may hold padding, so its scale is 0 (the dwords are always read
+      // and masked as bits: no branch and wait around each LDS read)
+      const uint32_t gmask = g < groups ? 0xFFFFu : 0u;
+      const int shift = wk ? 16 : 0;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const i32x4 sd = *(const i32x4*)(sS + wn * BNW + tn * 16 + 4 * og);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[tn][r] = f16_bits_to_f32((uint16_t)(((uint32_t)sd[r] >> shift) & gmask));
+      }
+      // asymmetric: the zero point of the lane's B row (the MFMA's first
+      // operand row, i.e. column n)
+      uint32_t zb[TN];
+      if constexpr (ZP) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const uint32_t zd = sZ[wn * BNW + tn * 16 + orow];
+          zb[tn] = c128 | (((zd >> (8 * (g & 3))) & 0xFu) * 0x00010001u);
+        }
+      }
+      f32x4 Z[ZP ? TN : 1][MT];
+      f32x4 Zc = {};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // A fragments: k chunk 4g + j of rows orow of each m-tile, permuted to
-        // the element order {0,4,1,5,2,6,3,7} the B dequant produces
+        // A fragments: k chunk 16 wk + 4 og + j of rows orow of each m-tile
         i32x4 af[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int row = mt * 16 + orow;
-          const int c = 4 * og + j;
-          const i32x4 d = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ (row & 15)) << 4));
-          af[mt] = i32x4{(int)__builtin_amdgcn_perm((uint32_t)d[2], (uint32_t)d[0], 0x05040100u),
-                         (int)__builtin_amdgcn_perm((uint32_t)d[2], (uint32_t)d[0], 0x07060302u),
-                         (int)__builtin_amdgcn_perm((uint32_t)d[3], (uint32_t)d[1], 0x05040100u),
-                         (int)__builtin_amdgcn_perm((uint32_t)d[3], (uint32_t)d[1], 0x07060302u)};
+          const int c = wk * 16 + 4 * og + j;
+          af[mt] = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ (row & 15)) << 4));
+        }
+        if constexpr (ZP) {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const i32x4 bz = {(int)zb[tn], (int)zb[tn], (int)zb[tn], (int)zb[tn]};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) Z[tn][mt] = mfma16_bf16(bz, af[mt], j == 0 ? f32x4{} : Z[tn][mt]);
+          }
+        } else {
+          // the same LDS bytes as af[wn % MT] (only known at run time); every
+          // wave runs the chain so that the loop body has no branch, and the
+          // waves with wn < MT publish it
+          const i32x4 bz = {(int)zsym, (int)zsym, (int)zsym, (int)zsym};
+          const int row = (wn % MT) * 16 + orow;
+          const int c = wk * 16 + 4 * og + j;
+          const i32x4 am = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ (row & 15)) << 4));
+          Zc = mfma16_bf16(bz, am, Zc);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) R[mt] = mfma16_bf16(ones, af[mt], j == 0 ? f32x4{} : R[mt]);
-#pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const uint32_t q = (uint32_t)bw[tn][j];
-          // bf16 pairs (128 + q_i, 128 + q_{i+4}) for i = 0..3: one bitfield
-          // insert per dword
-          const i32x4 bq = {(int)nib_bf16(q, m4, c128), (int)nib_bf16(q >> 4, m4, c128),
-                            (int)nib_bf16(q >> 8, m4, c128), (int)nib_bf16(q >> 12, m4, c128)};
+          const uint32_t q = (uint32_t)bw[tn][j], y = q >> 4;
+          const i32x4 bq = {(int)nib_bf16(__builtin_amdgcn_perm(y, q, kSel0), m4, c128),
+                            (int)nib_bf16(__builtin_amdgcn_perm(y, q, kSel1), m4, c128),
+                            (int)nib_bf16(__builtin_amdgcn_perm(y, q, kSel2), m4, c128),
+                            (int)nib_bf16(__builtin_amdgcn_perm(y, q, kSel3), m4, c128)};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) P[tn][mt] = mfma16_bf16(bq, af[mt], j == 0 ? f32x4{} : P[tn][mt]);
         }
+        // VALU work handed in by the caller, placed between the k-steps so
+        // that it runs while this step's MFMAs do
+        hook(j);
       }
-      // acc += s_n * (P - (128 + zp) * R); lane holds columns n = 4*og + r of each n-tile
-      const int half = kt & 1;
-      const uint32_t* sZ = (const uint32_t*)((const char*)sS + Cfg::S_BYTES);
-      auto correct = [&](auto with_z) {
+      if constexpr (ZP) {
+        // zero points per column: the correction right away
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          float s[4], zo[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t dw = sS[w * 64 + tn * 16 + 4 * og + r];
-            s[r] = f16_bits_to_f32((uint16_t)(half ? dw >> 16 : dw & 0xFFFF));
-            if constexpr (decltype(with_z)::value)
-              zo[r] = 128.0f + (float)((sZ[w * 64 + tn * 16 + 4 * og + r] >> (8 * (kt & 3))) & 0xFFu);
-            else
-              zo[r] = zoff;
-          }
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              acc.v[tn][mt][r] = __builtin_fmaf(s[r], __builtin_fmaf(-zo[r], R[mt][r], P[tn][mt][r]), acc.v[tn][mt][r]);
-        }
-      };
-      // uniform branch: the symmetric case reads no zero points
-      if (has_z)
-        correct(std::true_type{});
-      else
-        correct(std::false_type{});
+              acc.v[tn][mt][r] = __builtin_fmaf(sc[tn][r], P[tn][mt][r] - Z[tn][mt][r], acc.v[tn][mt][r]);
+      } else {
+        // lane (og, orow) holds Z of row orow (every output column of the
+        // chain carries the same value); each lane writes its own copy, so
+        // no lane is masked off (a branch would split the scheduling region)
+        zx[zslot(kt, wk, og) + orow * MT + wn % MT] = Zc[0];
+      }
     };
+    // symmetric: acc += s_n * (P - Z) for the group computed in the previous
+    // k-tile (Z from the exchange)
+    auto zread = [&](int kt, float (&zv)[MT]) {
+      const float* zr = zx + zslot(kt, wk, og) + orow * MT;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) zv[mt] = zr[mt];
+    };
+    auto correct_mt = [&](int mt, const f32x4 (&P)[TN][MT], const float (&sc)[TN][4], const float (&zv)[MT]) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc.v[tn][mt][r] = __builtin_fmaf(sc[tn][r], P[tn][mt][r] - zv[mt], acc.v[tn][mt][r]);
+    };
+    auto correct = [&](const f32x4 (&P)[TN][MT], const float (&sc)[TN][4], const float (&zv)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) correct_mt(mt, P, sc, zv);
+    };
+    auto no_hook = [](int) {};
 
     const int nk = u.ke - u.kb;
     constexpr int S = Cfg::STAGES;
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) issue(st, u.kb + st);
-    for (int it = 0; it < nk; ++it) {
-      wait_vmcnt<Cfg::LPW * (S - 2)>();
-      lds_barrier();
-      issue((it + S - 1) % S, u.kb + it + S - 1);
-      group(it % S, u.kb + it);
+    f32x4 P[TN][MT];
+    float sc[TN][4];
+    if (has_z) {
+      for (int it = 0; it < nk; ++it) {
+        wait_vmcnt<Cfg::LPW * (S - 2)>();
+        lds_barrier();
+        issue((it + S - 1) % S, u.kb + it + S - 1);
+        group(it % S, u.kb + it, std::true_type{}, P, sc, no_hook);
+      }
+    } else {
+      // the first iteration corrects a "previous group" of zeros: P = 0, s = 0
+      // and its Z slot zeroed (so that no stale LDS value turns 0 * x into NaN)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) P[tn][mt] = f32x4{};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[tn][r] = 0.f;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) zx[zslot(u.kb - 1, wk, og) + orow * MT + mt] = 0.f;
+      // one k-tile: correct the previous group (Pq, sq) while computing this
+      // one into (Pc, sc_); the loop below alternates two register sets
+      // instead of copying them
+      auto step = [&](int it, f32x4 (&Pc)[TN][MT], float (&scc)[TN][4], const f32x4 (&Pq)[TN][MT],
+                      const float (&sq)[TN][4]) {
+        wait_vmcnt<Cfg::LPW * (S - 2)>();
+        lds_barrier();
+        // the previous group's Z values, read before this group writes the
+        // other half of the exchange (the compiler cannot tell them apart)
+        float zv[MT];
+        zread(u.kb + it - 1, zv);
+        issue((it + S - 1) % S, u.kb + it + S - 1);
+        // the previous group's correction (VALU) and this group's chains
+        // (MFMA) are independent: they are interleaved k-step by k-step so
+        // that both units stay busy; k-step j corrects m-tiles j, j + 4, ...
+        group(it % S, u.kb + it, std::false_type{}, Pc, scc, [&](int j) {
+#pragma unroll
+          for (int mt = j; mt < MT; mt += 4) correct_mt(mt, Pq, sq, zv);
+        });
+      };
+      f32x4 P2[TN][MT];
+      float sc2[TN][4];
+      int it = 0;
+      for (; it + 1 < nk; it += 2) {
+        step(it, P2, sc2, P, sc);
+        step(it + 1, P, sc, P2, sc2);
+      }
+      if (it < nk) {
+        step(it, P2, sc2, P, sc);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) P[tn][mt] = P2[tn][mt];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[tn][r] = sc2[tn][r];
+        }
+      }
     }
     wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the ring before it is reused below
+    if (!has_z && nk > 0) {
+      float zv[MT];
+      zread(u.ke - 1, zv);
+      correct(P, sc, zv);
+    }
+
+    // Add the k-group partial sums in wk order into the wk = 0 waves.
+    f32x4* red = (f32x4*)smem;
+    if (wk > 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[((((wk - 1) * WN + wn) * TN + tn) * MT + mt) * 64 + l] = acc.v[tn][mt];
+    }
     __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] += red[((((k2 - 1) * WN + wn) * TN + tn) * MT + mt) * 64 + l];
+    }
+    __syncthreads();  // the ring is reused by the next unit
   }
 
-  // Lane holds D[m][n .. n+3] with m = 16 mt + l%16, n = n0 + w*BNW + 16 tn + 4 (l/16).
+  // Lane holds D[m][n .. n+3] with m = 16 mt + l%16, n = n0 + wn*BNW + 16 tn + 4 (l/16).
   __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* /*smem*/) {
     const int w = wave_id(), l = lane_id();
+    if (wk_of(w) != 0) return;
+    const int wn = wn_of(w);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = u.m0 + mt * 16 + (l & 15);
       if (m >= u.m_end) continue;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int n = u.n0 + w * Cfg::BNW + tn * 16 + 4 * (l >> 4);
+        const int n = u.n0 + wn * BNW + tn * 16 + 4 * (l >> 4);
         if (n < a.N) epi_store4(a, m, n, acc.v[tn][mt]);
       }
     }
@@ -254,10 +422,12 @@ struct W4 {
   __device__ __forceinline__ static __amdgpu_buffer_rsrc_t slot_rsrc(const Args& a, int slot) {
     return make_rsrc((const char*)a.partials + (size_t)slot * (BM * BN * 4), BM * BN * 4);
   }
+  // Partial tile layout: [wn][tn][mt][lane] x 16 bytes (written by the wk = 0 waves).
   __device__ __forceinline__ static uint32_t pofs(int tn, int mt) {
-    return (uint32_t)((((wave_id() * TN + tn) * MT + mt) * 64 + lane_id()) * 16);
+    return (uint32_t)((((wn_of(wave_id()) * TN + tn) * MT + mt) * 64 + lane_id()) * 16);
   }
   __device__ __forceinline__ static void write_partial(const Args& a, int slot, Acc& acc) {
+    if (wk_of(wave_id()) != 0) return;
     const auto r = slot_rsrc(a, slot);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
@@ -267,7 +437,7 @@ struct W4 {
   // Chunk c = tn * MT + mt of a lane's partial tile.
   using S4 = f32x4;
   static constexpr int NCH = TN * MT;
-  __device__ __forceinline__ static bool holds_partial() { return true; }
+  __device__ __forceinline__ static bool holds_partial() { return wk_of(wave_id()) == 0; }
   __device__ __forceinline__ static uint32_t chunk_off(int c) { return pofs(c / MT, c % MT); }
   __device__ __forceinline__ static S4 get4(const Acc& acc, int c) { return acc.v[c / MT][c % MT]; }
   __device__ __forceinline__ static void set4(Acc& acc, int c, const S4& x) { acc.v[c / MT][c % MT] = x; }

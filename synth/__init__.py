@@ -208,18 +208,28 @@ def w8a8_problem(M, N, K, out_dtype=BF16, c_dtype=None, alpha=1.0, beta=0.0, see
 
 
 def w4a16_problem(M, N, K, group=128, seed=SEED_A, out_dtype=BF16, a_std=1.0,
-                  s_lo=0.005, s_hi=0.02, zero_point=8, asym=False):
+                  s_lo=0.005, s_hi=0.02, zero_point=8, asym=False, zp_cols=(), zp_groups=()):
     """A bf16 [M,K] ~ N(0,a_std); B int4 nibbles uniform 0..15 packed [N, K/8];
     V fp16 scales [N, K/group] ~ U[s_lo, s_hi]; asym: per-group zero points
-    Z int8 [N, K/group] uniform 0..15 instead of the constant zero_point."""
+    Z int8 [N, K/group] uniform 0..15 instead of the constant zero_point.
+    zp_cols / zp_groups (column, group): nibbles set equal to the column's
+    zero point over the whole column / one group (weights that dequantise to
+    zero, as in pruned output channels)."""
     a = normal((M, K), a_std, seed)
     q = rng(seed + 1).integers(0, 16, size=(N, K), dtype=np.int64)
-    s = uniform((N, -(-K // group)), s_lo, s_hi, seed + 3)
+    G = -(-K // group)
+    s = uniform((N, G), s_lo, s_hi, seed + 3)
+    z = rng(seed + 5).integers(0, 16, size=(N, G), dtype=np.int64) if asym else np.full((N, G), zero_point)
+    for n in zp_cols:
+        for g in range(G):
+            q[n, g * group:(g + 1) * group] = z[n, g]
+    for (n, g) in zp_groups:
+        q[n, g * group:(g + 1) * group] = z[n, g]
     p = dict(kind="w4a16", M=M, N=N, K=K, in_dtype=BF16, out_dtype=out_dtype, c_dtype=None,
              alpha=1.0, beta=0.0, group=group, zero_point=zero_point,
              A=to_bf16_bits(a), B=pack_int4(q), V=to_f16_bits(s))
     if asym:
-        p["Z"] = rng(seed + 5).integers(0, 16, size=(N, -(-K // group)), dtype=np.int64).astype(np.int8)
+        p["Z"] = z.astype(np.int8)
     return p
 
 

@@ -314,7 +314,7 @@ def test_w4a16_validation(g):
     assert run(g, op=q, Ad=qg.layout("f16", M, K), Bd=Bd, Dd=Dd, V=FAKE, Vd=Vd) == qg.ERR_UNSUPPORTED
     # a valid request plans onto the int4 kernel with split-K
     d = dict(kv.split("=") for kv in g.plan(q, Ad, None, Bd, Vd, None, Dd, 1.0, 0.0, ws_desc()).split())
-    assert d["kernel"].startswith("w4_BF16_") and d["bk"] == "128"
+    assert d["kernel"].startswith("w4_BF16_") and d["bk"] == "256"
 
 
 def test_fp8_block_scaled_validation(g):
