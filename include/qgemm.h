@@ -26,7 +26,11 @@
  *     memory (the measure policy allocates nothing either; it synchronises).
  *   - Accumulation is fp32 for float inputs and exact int32 for int8.
  *   - Alignment: every device pointer and every row pitch (ld * element size)
- *     must be a multiple of 16 bytes; K must keep rows 16-byte aligned too.
+ *     must be a multiple of 16 bytes. K need not be: a row of A or B is read
+ *     in 16-byte chunks up to the first 16-byte boundary at or past its K-th
+ *     element, which lies inside the row pitch (so the storage of the last
+ *     row must reach that boundary; rows x ld elements always do). Whatever
+ *     those bytes past K hold (NaN included) is zeroed on chip before use.
  *
  * Threading: one handle may be used from several host threads except under
  * QG_POLICY_MEASURE (which mutates the dispatch cache and synchronises the

@@ -69,6 +69,26 @@ __device__ __forceinline__ void load_lds_x1a(const i32x4& rsrc, void* lds_wave_b
       : "memory", "m0");
 }
 
+// Zeroes, in LDS, the bytes of a 16-byte chunk from byte `keep` on
+// (0 < keep < 16). When K * element size is not a multiple of 16, the chunk
+// that holds the end of a row's K elements also holds bytes past K (row
+// padding with undefined contents, possibly NaN); they must read as zero
+// before any MFMA consumes the chunk, as out-of-range chunks do. Called by
+// the lane whose direct load wrote the chunk, after waiting for that load;
+// the caller's barrier (or, within one wave, LDS ordering) publishes it.
+__device__ __forceinline__ void lds_chunk_trim(char* p, int keep) {
+  asm volatile("" ::: "memory");
+  i32x4 x = *(const i32x4*)p;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int vb = keep - 4 * d;  // bytes of dword d that lie before K
+    const uint32_t m = vb >= 4 ? ~0u : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+    x[d] = (int)((uint32_t)x[d] & m);
+  }
+  *(i32x4*)p = x;
+  asm volatile("" ::: "memory");
+}
+
 // 16-byte buffer store / load with the sc1 cache-policy bit (coherent at agent
 // scope across the XCDs' L2s; gfx950 cache-policy encoding: sc0 = 1, nt = 2,
 // sc1 = 16).

@@ -331,7 +331,9 @@ int validate(const qg_operation* op, float alpha, const void* A, const qg_layout
   if (p.lda < p.K || b_row_elems < p.K || p.ldd < p.N) return QG_ERR_INVALID_ARG;
   if (p.tb == QG_U4 && p.K % 8) return QG_ERR_ALIGNMENT;
   if ((p.lda * esize(p.ta)) % 16 || (p.ldb * esize(p.tb)) % 16 || (p.ldd * esize(p.td)) % 16) return QG_ERR_ALIGNMENT;
-  if ((p.K * esize(p.ta)) % 16) return QG_ERR_ALIGNMENT;
+  // K itself need not keep rows 16-byte aligned: the kernels read a row's
+  // last partial 16-byte chunk whole (it lies inside the row pitch) and zero
+  // its bytes past K on chip
   if (!aligned16(A) || !aligned16(B) || !aligned16(D)) return QG_ERR_ALIGNMENT;
   if (grouped) {
     p.b_batch = Bd->stride;  // 0: every group uses the same B

@@ -103,6 +103,24 @@ struct F8 : Tile<Cfg> {
       load_lds_x1a(rS, sbase + Cfg::STAGE_BYTES + w * 256, live && s_lane ? offS + (uint32_t)kt * 4 : kOOB);
     };
 
+    // K not a multiple of 16: zero the bytes past K in the chunks this lane
+    // loaded for the k-tile that holds K's end (as in the tile core).
+    const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / 128) : -1;
+    auto trim = [&](int stage, int kt) {
+      char* sbase = smem + stage * Cfg::STAGE8;
+      const uint32_t kk = (uint32_t)kt * 128;
+#pragma unroll
+      for (int i = 0; i < Cfg::LA; ++i) {
+        const int keep = (int)(kbytes - kk - chA[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(sbase + (w * Cfg::LA + i) * 1024 + l * 16, keep);
+      }
+#pragma unroll
+      for (int i = 0; i < Cfg::LB; ++i) {
+        const int keep = (int)(kbytes - kk - chB[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024 + l * 16, keep);
+      }
+    };
+
     // Fragments of one 64-deep k-step: lane l takes row l % 32 and the 32
     // contiguous bytes of k selected by l / 32, for A and B alike.
     const int orow = l & 31, ohalf = l >> 5;
@@ -139,6 +157,7 @@ struct F8 : Tile<Cfg> {
 #pragma unroll
     for (int st = 0; st < S; ++st) issue(st, u.kb + st);
     wait_vmcnt<Cfg::LPW8 * (S - 1)>();
+    if (u.kb == ktail) trim(0, ktail);
     lds_barrier();
     for (int it = 0; it < nk; ++it) {
       const int st = it % S;
@@ -164,6 +183,7 @@ struct F8 : Tile<Cfg> {
       // every wave has read stage st (fragments and scales): refill it with
       // k-tile it + S; the wait makes stage it + 1 resident for the next step
       wait_vmcnt<Cfg::LPW8 * (S - 2)>();
+      if (u.kb + it + 1 == ktail) trim((it + 1) % S, ktail);
       lds_barrier();
       issue(st, u.kb + it + S);
 #pragma unroll

@@ -157,6 +157,24 @@ struct Skinny {
       for (int i = 0; i < LA; ++i)
         load_lds_x4(rA, base + BNW * Cfg::BLKB + i * 1024, live && kk + chA[i] < kbytes ? offA[i] + kk : kOOB);
     };
+    // K * ESIZE not a multiple of 16: in the block that holds K's end, zero
+    // the bytes past K in the chunks this lane loaded (its own loads have
+    // landed; the wave's LDS accesses stay in order, so its reads see this).
+    const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / Cfg::BLKB) : -1;
+    auto trim = [&](int d, int blk) {
+      char* base = ring + d * Cfg::SLOT;
+      const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        const int keep = (int)(kbytes - kk - chB[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(base + i * 1024 + l * 16, keep);
+      }
+#pragma unroll
+      for (int i = 0; i < LA; ++i) {
+        const int keep = (int)(kbytes - kk - chA[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(base + BNW * Cfg::BLKB + i * 1024 + l * 16, keep);
+      }
+    };
     // Operand fragments of the block in slot d: step j covers bytes
     // [64j, 64j+64) of each row; lane l reads row l%16 of each 16-row group at
     // logical chunk 4j + l/16.
@@ -210,6 +228,10 @@ struct Skinny {
       for (int d = 0; d < DEPTH; ++d) {
         wait_vmcnt<Cfg::LPS * (DEPTH - 1)>();
         asm volatile("" ::: "memory");
+        {
+          const int blk = u.kb + kfirst + (r * DEPTH + d) * KSTRIDE;
+          if (blk == ktail) trim(d, blk);
+        }
         read(d);
         // refill the slot as soon as its fragments are in registers
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -285,6 +307,22 @@ struct Skinny {
       for (int i = 0; i < LB; ++i) load_lds_x4(rB, base + i * 1024, live && kk + chB[i] < kbytes ? offB[i] + kk : kOOB);
       load_lds_x4(rA, aring + d * Cfg::ASLOT + ia * 1024, live && kk + chA < kbytes ? offA + kk : kOOB);
     };
+    // K * ESIZE not a multiple of 16: zero the bytes past K in the chunks
+    // this lane loaded for the block that holds K's end, before the barrier
+    // that publishes the block. Waves that load the same A chunk each trim it
+    // after their own copy has landed, so the last write is a trimmed one.
+    const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / Cfg::BLKB) : -1;
+    auto trim = [&](int d, int blk) {
+      char* base = bring + d * Cfg::SLOT;
+      const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        const int keep = (int)(kbytes - kk - chB[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(base + i * 1024 + l * 16, keep);
+      }
+      const int keep = (int)(kbytes - kk - chA);
+      if (keep > 0 && keep < 16) lds_chunk_trim(aring + d * Cfg::ASLOT + ia * 1024 + l * 16, keep);
+    };
     i32x4 fb[ST][TN], fa[ST][MT];
     auto read = [&](int d) {
       const char* bb = bring + d * Cfg::SLOT;
@@ -319,6 +357,7 @@ struct Skinny {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
         wait_vmcnt<Cfg::LPS * (DEPTH - 2)>();
+        if (u.kb + r * DEPTH + d == ktail) trim(d, ktail);
         lds_barrier();
         issue((d + DEPTH - 1) % DEPTH, u.kb + r * DEPTH + d + DEPTH - 1);
         read(d);

@@ -320,6 +320,26 @@ struct Tile {
       }
     };
 
+    // K * ESIZE not a multiple of 16: the k-tile `ktail` holds each row's
+    // chunk that straddles K. Once this lane's loads of that k-tile have
+    // landed (and before the barrier that publishes the stage), it zeroes the
+    // bytes past K in the chunks it loaded.
+    const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / ROWB) : -1;
+    auto trim = [&](int stage, int kt) {
+      char* sbase = smem + stage * Cfg::STAGE_BYTES;
+      const uint32_t kk = (uint32_t)kt * ROWB;
+#pragma unroll
+      for (int i = 0; i < Cfg::LA; ++i) {
+        const int keep = (int)(kbytes - kk - chA[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(sbase + (w * Cfg::LA + i) * 1024 + l * 16, keep);
+      }
+#pragma unroll
+      for (int i = 0; i < Cfg::LB; ++i) {
+        const int keep = (int)(kbytes - kk - chB[i]);
+        if (keep > 0 && keep < 16) lds_chunk_trim(sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024 + l * 16, keep);
+      }
+    };
+
     // MFMA operand fragments of one k-step, read from LDS.
     const int orow = l & 31, ohalf = l >> 5;
     struct Frags {
@@ -374,6 +394,7 @@ struct Tile {
 #pragma unroll
     for (int st = 0; st < S; ++st) issue(st, u.kb + st);
     wait_vmcnt<Cfg::LPW * (S - 1)>();
+    if (u.kb == ktail) trim(0, ktail);
     lds_barrier();
     Frags cur;
     read_frags(0, 0, cur);
@@ -394,6 +415,7 @@ struct Tile {
           // are read while the other half of the MFMAs run.
           mma(cur, 0, TN / 2);
           wait_vmcnt<Cfg::LPW * (S - 2)>();
+          if (u.kb + it + 1 == ktail) trim((it + 1) % S, ktail);
           lds_barrier();
           issue(st, u.kb + it + S);
           read_frags((it + 1) % S, 0, nxt);

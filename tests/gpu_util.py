@@ -40,16 +40,39 @@ def kind_of(p):
     return p["kind"]
 
 
+# What the row padding past K holds when a test stores A and B with ld > K:
+# NaN codes for the float formats (a NaN that reached an MFMA would poison the
+# output), and for int8 extreme values of opposite sign in A and B (a product
+# of two unmasked padding bytes adds -16256 to the sum).
+_PAD_A = {"bf16": 0x7FC0, "f16": 0x7E00, "e4m3": 0x7F, "i8": 127}
+_PAD_B = {"bf16": 0x7FC0, "f16": 0x7E00, "e4m3": 0x7F, "i8": -128}
+
+
+def pad_k(x, ldk, fill):
+    """Copy of x (last axis K) with rows of ldk elements; elements K..ldk-1 hold `fill`."""
+    out = np.full(x.shape[:-1] + (ldk,), fill, dtype=x.dtype)
+    out[..., :x.shape[-1]] = x
+    return out
+
+
 class Run:
     """Uploads a problem once; `run(op)` launches and returns D on the host."""
 
-    def __init__(self, gemm, p, ws=None, out_dtype=None):
+    def __init__(self, gemm, p, ws=None, out_dtype=None, ldk=None):
+        """ldk: row pitch of A and B in elements (dense and grouped problems),
+        with the padding past K filled with NaN codes / extreme int8 values."""
         self.g, self.p = gemm, p
         self.ws = ws
         self.out = out_dtype or p["out_dtype"]
         M, N, K = p["M"], p["N"], p["K"]
-        self.A = dev(p["A"])
-        self.B = dev(p["B"])
+        self.ldk = ldk or K
+        if ldk:
+            assert p["kind"] in ("dense", "grouped") and not p.get("batched") and ldk >= K
+            self.A = dev(pad_k(p["A"], ldk, _PAD_A[p["in_dtype"]]))
+            self.B = dev(pad_k(p["B"], ldk, _PAD_B[p["in_dtype"]]))
+        else:
+            self.A = dev(p["A"])
+            self.B = dev(p["B"])
         # C and D rows are padded to a 16-byte row pitch (8 elements; 16 for int8 D)
         self.ldn = -(-N // 16) * 16 if self.out == "i8" else -(-N // 8) * 8
         self.C = None
@@ -88,13 +111,13 @@ class Run:
         elif kind == "grouped":
             E = p["E"]
             self.off = dev(np.asarray(p["offsets"], dtype=np.int32))
-            self.Ad = qg.layout(p["in_dtype"], M, K, num=E, offsets=self.off.data_ptr())
-            self.Bd = qg.layout(p["in_dtype"], N, K, num=E, stride=N * K)
+            self.Ad = qg.layout(p["in_dtype"], M, K, ld=self.ldk, num=E, offsets=self.off.data_ptr())
+            self.Bd = qg.layout(p["in_dtype"], N, K, ld=self.ldk, num=E, stride=N * self.ldk)
             self.Dd = qg.layout(self.out, M, N, ld=self.ldn, num=E, offsets=self.off.data_ptr())
         else:
             bt = "u4" if kind == "w4a16" else p["in_dtype"]
-            self.Ad = qg.layout(p["in_dtype"], M, K)
-            self.Bd = qg.layout(bt, N, K)
+            self.Ad = qg.layout(p["in_dtype"], M, K, ld=self.ldk)
+            self.Bd = qg.layout(bt, N, K, ld=self.ldk if bt != "u4" else None)
             self.Dd = qg.layout(self.out, M, N, ld=self.ldn)
         self.Cd = qg.layout(p["c_dtype"], M, N, ld=self.ldn) if self.C is not None else None
         if p.get("batched") and self.C is not None:

@@ -89,6 +89,20 @@ def test_alignment(g):
     assert run(g, Ad=qg.layout("bf16", 64, 64, ld=68), Bd=Bd, Dd=Dd) == qg.ERR_ALIGNMENT
 
 
+@pytest.mark.parametrize("t, K, ld", [("bf16", 100, 104), ("f16", 6, 8), ("i8", 40, 48), ("i8", 1, 16)])
+def test_k_need_not_fill_16_byte_chunks(g, t, K, ld):
+    # only pointers and row pitches must be 16-byte aligned: a K whose last
+    # chunk is partial is planned like any other (its bytes past K are zeroed
+    # on chip)
+    out = "i32" if t == "i8" else "bf16"
+    Ad, Bd, Dd = qg.layout(t, 64, K, ld=ld), qg.layout(t, 96, K, ld=ld), qg.layout(out, 64, 96, ld=96)
+    assert "kernel=" in g.plan(qg.operation(), Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc())
+    # ...but the pitch still has to be
+    with pytest.raises(RuntimeError):
+        g.plan(qg.operation(), qg.layout(t, 64, K, ld=K), None, qg.layout(t, 96, K, ld=K), None, None, Dd, 1.0,
+               0.0, ws_desc())
+
+
 def test_unsupported(g):
     Ad, Bd, Dd = dense(64, 64, 64)
     assert run(g, Ad=qg.layout("bf16", 64, 64, order=qg.COL_MAJOR), Bd=Bd, Dd=Dd) == qg.ERR_UNSUPPORTED
