@@ -19,7 +19,23 @@ block-scaled fp8) are reported under "w4a16", "moe" and "moe_fp8".
 its mean launch time, measured with HIP events on the launch stream, against
 the dense bf16 MFMA peak (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s).
 `cpu_baseline` times the fp64 CPU oracle on a bounded row sample of the same
-problem on this host's cores.
+problem on this host's cores; `cpu_oracle` times it on every workload (a
+row sample where the whole product would take minutes), with the CPU model,
+the cores this process may run on, and a single-threaded run of the small
+256^3 case.
+
+Measured in the same process, next to the kernels they bound (`ceilings`):
+an MFMA-only loop at the 4096^3 kernel's occupancy (the sustained matrix
+rate, and the shader clock it ran at, from s_memtime / s_memrealtime) and a
+streaming read of the decode weight's size (the sustained HBM read rate);
+`frac_of_sustained` / `frac_of_stream` place the kernels against them.
+`clocks` holds the shader / memory clock and board power read from sysfs
+while each workload's timed graph is replayed for about a second
+(`sustained_us` is the mean kernel time over that second).
+`host_us_per_call` is the host time of one qg_run on the decode problem
+(a C loop of back-to-back calls): with the DEFAULT policy (memoised
+heuristic), after MEASURE (dispatch-cache hit), FORCE, and the runtime's
+cost of launching an empty kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -30,7 +46,10 @@ import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +83,146 @@ def traffic_from_profile(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def log(msg):
+    """Progress of the run on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def graph_time(step, steps, warmup):
+    """Warm up eagerly, capture `steps` calls of step(i) in one HIP graph and
+    time its replay with HIP events on the launch stream (no host gaps between
+    launches, so the per-launch figure is device time). Returns the timing and
+    the graph (for sustain())."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()  # warm replay
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total = e0.elapsed_time(e1)
+    return dict(total_ms=total, wall_s=wall, kernel_ms_mean=total / steps), graph
+
+
+def _sysfs_device():
+    """sysfs directory of device 0 (by PCI address), or of the only amdgpu card."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    bus, dev, dom = (getattr(pr, k, None) for k in ("pci_bus_id", "pci_device_id", "pci_domain_id"))
+    if bus is not None and dev is not None:
+        path = f"/sys/bus/pci/devices/{int(dom or 0):04x}:{int(bus):02x}:{int(dev):02x}.0"
+        if os.path.isdir(path):
+            return path
+    cards = {os.path.realpath(os.path.dirname(f)) for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")}
+    return cards.pop() if len(cards) == 1 else None
+
+
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read()
+    except OSError:
+        return None
+
+
+def _dpm_mhz(text):
+    """Current level of a pp_dpm_* table ('1: 2400Mhz *')."""
+    for line in (text or "").splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+            if m:
+                return float(m.group(1))
+    return None
+
+
+class ClockSampler:
+    """Reads the shader clock, memory clock and board power of device 0 from
+    sysfs every few milliseconds on a background thread."""
+
+    def __init__(self, dev, period_s=0.004):
+        self.dev, self.period = dev, period_s
+        self.samples = {"sclk_mhz": [], "mclk_mhz": [], "power_w": []}
+        self._stop = threading.Event()
+        self._files = {}
+        if dev:
+            hw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*")))
+            for key, names in (("sclk_hz", ["freq1_input"]), ("power_uw", ["power1_average", "power1_input"])):
+                for h in hw:
+                    f = next((os.path.join(h, n) for n in names if os.path.exists(os.path.join(h, n))), None)
+                    if f:
+                        self._files[key] = f
+                        break
+            for key in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                if os.path.exists(os.path.join(dev, key)):
+                    self._files[key] = os.path.join(dev, key)
+
+    def _sample(self):
+        f = self._files
+        v = _read(f["sclk_hz"]) if "sclk_hz" in f else None
+        sclk = float(v) / 1e6 if v and v.strip().isdigit() else (_dpm_mhz(_read(f["pp_dpm_sclk"]))
+                                                                if "pp_dpm_sclk" in f else None)
+        mclk = _dpm_mhz(_read(f["pp_dpm_mclk"])) if "pp_dpm_mclk" in f else None
+        v = _read(f["power_uw"]) if "power_uw" in f else None
+        power = float(v) / 1e6 if v and v.strip().isdigit() else None
+        for k, x in (("sclk_mhz", sclk), ("mclk_mhz", mclk), ("power_w", power)):
+            if x is not None:
+                self.samples[k].append(x)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            self._sample()
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self._t = threading.Thread(target=self._loop, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        if not self.dev:
+            return {"unavailable": "no sysfs directory found for device 0"}
+        out = {"n": len(self.samples["sclk_mhz"]), "source": {k: v for k, v in self._files.items()}}
+        for k, xs in self.samples.items():
+            if xs:
+                out[k] = {"mean": round(statistics.mean(xs), 1), "min": round(min(xs), 1), "max": round(max(xs), 1)}
+            else:
+                out[k] = None
+        return out
+
+
+def sustain(graph, steps, per_kernel_ms, dev, seconds=1.0):
+    """Replays a captured graph of `steps` launches back to back for about
+    `seconds` while sampling clocks and power; returns the mean kernel time
+    over that stretch and the sample summary."""
+    import torch
+    n = max(1, int(round(seconds * 1e3 / max(per_kernel_ms * steps, 1e-3))))
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with ClockSampler(dev) as cs:
+        e0.record(stream)
+        for _ in range(n):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return dict(sustained_us=round(e0.elapsed_time(e1) * 1e3 / (n * steps), 3), replays=n, **cs.summary())
+
+
 class Workload:
     """Rotating device input sets for one problem and a bound qg_run call.
     With same_data, one problem is generated and uploaded `nsets` times (the
@@ -82,56 +241,159 @@ class Workload:
         self.op = op if op is not None else self.runs[0].op()
         self.qg = qg
         self.torch = torch
+        self.graph = None
 
     def step(self, i):
         st = self.runs[i % len(self.runs)].launch(self.op)
         if st != self.qg.OK:
             raise self.qg.QGemmError(st, "qg_run")
 
-    def time(self, steps, warmup):
-        """Warm up eagerly, capture `steps` qg_run calls in one HIP graph and time
-        its replay with HIP events on the launch stream (no host gaps between
-        launches, so the per-launch figure is device time)."""
-        torch = self.torch
-        for i in range(warmup):
-            self.step(i)
+    def time(self, steps, warmup, dev=None):
+        t, self.graph = graph_time(self.step, steps, warmup)
+        if dev is not False:
+            t["clocks"] = sustain(self.graph, steps, t["kernel_ms_mean"], dev)
+        return t
+
+
+def ceiling_mfma(dev, grid=256, iters=2048, steps=20):
+    """MFMA-only loop at one 8-wave workgroup per CU: sustained bf16 rate and
+    the shader clock measured inside the loop."""
+    import torch
+    from quantized_gemm_bf16_amd import ceiling as qc
+    sink = torch.empty(grid, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    t, graph = graph_time(lambda i: qc.mfma_loop(grid, iters, sink, clk), steps, 3)
+    flops = grid * (qc.MFMA_THREADS // 64) * iters * qc.MFMA_FLOPS_PER_ROUND
+    c = clk.view(-1, 2).cpu().double()
+    sclk_ghz = float(c[:, 0].sum() / c[:, 1].sum()) * 0.1  # s_memrealtime ticks at 100 MHz
+    tflops = flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    cl = sustain(graph, steps, t["kernel_ms_mean"], dev, seconds=0.5) if dev is not False else None
+    return {"tflops": round(tflops, 1), "kernel_us_mean": round(t["kernel_ms_mean"] * 1e3, 3),
+            "flops_per_launch": flops, "shader_clock_ghz_in_loop": round(sclk_ghz, 3),
+            "flops_per_clk_per_cu": round(tflops * 1e12 / (sclk_ghz * 1e9 * 256), 1),
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "shape": f"{grid} workgroups x 8 waves x {iters} rounds of 4 v_mfma_f32_32x32x16_bf16", "clocks": cl}
+
+
+def ceiling_stream(dev, nbytes, nsets=3, steps=30):
+    """Streaming read of `nbytes` (rotating `nsets` buffers, together beyond
+    the 256 MB Infinity Cache); the best of a few grid sizes."""
+    import torch
+    from quantized_gemm_bf16_amd import ceiling as qc
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(nsets)]
+    blocks = -(-nbytes // qc.STREAM_BLOCK_BYTES)
+    best = None
+    for grid in sorted({blocks, -(-blocks // 2), 1024, 2048}):
+        sink = torch.empty(grid * qc.STREAM_THREADS, dtype=torch.int32, device="cuda")
+        t, graph = graph_time(lambda i: qc.stream_read(bufs[i % nsets], nbytes, grid, sink), steps, 3)
+        gbs = nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+        if best is None or gbs > best["GB/s"]:
+            best = {"GB/s": round(gbs, 1), "kernel_us_mean": round(t["kernel_ms_mean"] * 1e3, 3), "grid": grid,
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "graph": graph, "ms": t["kernel_ms_mean"]}
+    graph, ms = best.pop("graph"), best.pop("ms")
+    best["clocks"] = sustain(graph, steps, ms, dev, seconds=0.5) if dev is not False else None
+    best["bytes_per_launch"] = nbytes
+    return best
+
+
+def host_timing(g, ws, n=500):
+    """Host microseconds per qg_run on the decode problem (M=16), from a C loop
+    of n back-to-back calls; median of three loops."""
+    import torch
+    import quantized_gemm_bf16_amd as qg
+    from quantized_gemm_bf16_amd import ceiling as qc
+    import synth
+    from tests.gpu_util import Run
+    r = Run(g, synth.config_decode(M=16), ws)
+
+    def per_call(op):
+        r.launch(op)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(steps):
-                self.step(i)
-        graph.replay()  # warm replay
+        xs = []
+        for _ in range(3):
+            xs.append(qc.host_us_per_run(n, g, op, r.p["alpha"], r.A, r.Ad, r.U, r.Ud, r.B, r.Bd, r.V, r.Vd,
+                                         r.p["beta"], r.C, r.Cd, r.D, r.Dd, ws.desc))
+            torch.cuda.synchronize()
+        return round(statistics.median(xs), 3)
+
+    out = {"default_memo": per_call(qg.operation())}
+    st = r.launch(qg.operation(policy=qg.POLICY_MEASURE))
+    torch.cuda.synchronize()
+    if st == qg.OK:
+        out["cache_hit"] = per_call(qg.operation(policy=qg.POLICY_REUSE))
+    out["force"] = per_call(qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8))
+    xs = []
+    for _ in range(3):
+        xs.append(qc.host_us_per_empty(n))
         torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        total = e0.elapsed_time(e1)
-        return dict(total_ms=total, wall_s=wall, kernel_ms_mean=total / steps)
+    out["empty_kernel_launch"] = round(statistics.median(xs), 3)
+    out["calls_per_loop"] = n
+    out["problem"] = "decode M=16 N=4096 K=14336 bf16, C bf16, beta 1"
+    return out
+
+
+def cpu_model():
+    for line in (_read("/proc/cpuinfo") or "").splitlines():
+        if line.startswith("model name"):
+            return line.split(":", 1)[1].strip()
+    return None
+
+
+def oracle_time(p, rows=None):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.gemm(p, rows=rows)
+    return time.perf_counter() - t0
+
+
+def oracle_rows_time(p, nrows=None):
+    """The oracle (as it is) on a whole product, or on a seeded row sample
+    with the full time extrapolated by rows."""
+    import numpy as np
+    if nrows is None or nrows >= p["M"]:
+        return {"seconds": round(oracle_time(p), 3), "rows": "all"}
+    rows = sorted(set(np.random.default_rng(11).choice(p["M"], size=nrows, replace=False).tolist()))
+    dt = oracle_time(p, rows)
+    return {"seconds_sample": round(dt, 3), "rows": f"{len(rows)} of {p['M']}",
+            "seconds_full_estimate": round(dt * p["M"] / len(rows), 1)}
+
+
+def oracle_timings(configs):
+    """Host description and the oracle's time on the small 256^3 case (with
+    all threads and with one), merged with the per-workload timings."""
+    import oracle
+    import synth
+    out = {"cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+           "omp_threads": oracle.num_threads()}
+    tiny = synth.config_tiny()
+    cfg = {"tiny_256^3_f32": {"seconds": round(oracle_time(tiny), 4), "rows": "all"}}
+    prev = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        out["tiny_256^3_single_thread_s"] = round(oracle_time(tiny), 4)
+    finally:
+        oracle.set_num_threads(prev)
+    cfg.update(configs)
+    out["configs"] = cfg
+    return out
 
 
 def cpu_baseline(p, flops_per_row, target_s=15.0):
-    """The oracle, as it is, on a row sample sized to about `target_s` seconds."""
+    """The oracle, as it is, on a row sample sized to about `target_s` seconds.
+    Returns the cpu_baseline entry and the sample's timing."""
     import numpy as np
     import oracle
     rows = [0, 1]
-    t0 = time.perf_counter()
-    oracle.gemm(p, rows=rows)
-    dt = max(time.perf_counter() - t0, 1e-3)
+    dt = max(oracle_time(p, rows), 1e-3)
     n = int(min(p["M"], max(2, round(target_s / (dt / len(rows))))))
     rows = sorted(set(np.random.default_rng(7).choice(p["M"], size=n, replace=False).tolist()))
-    t0 = time.perf_counter()
-    oracle.gemm(p, rows=rows)
-    dt = time.perf_counter() - t0
-    return dict(value=len(rows) * flops_per_row / dt / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle",
-                sample=f"{len(rows)} of {p['M']} rows of the {p['M']}x{p['N']}x{p['K']} product "
-                       f"({len(rows) * p['N']} outputs, fp64, {dt:.1f} s)")
+    dt = oracle_time(p, rows)
+    entry = dict(value=len(rows) * flops_per_row / dt / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                 kind="oracle",
+                 sample=f"{len(rows)} of {p['M']} rows of the {p['M']}x{p['N']}x{p['K']} product "
+                        f"({len(rows) * p['N']} outputs, fp64, {dt:.1f} s)")
+    return entry, {"seconds_sample": round(dt, 3), "rows": f"{len(rows)} of {p['M']}",
+                   "seconds_full_estimate": round(dt * p["M"] / len(rows), 1)}
 
 
 def main():
@@ -139,10 +401,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["square", "decode", "w4a16", "moe", "moe_fp8"], default=None,
-                    help="time one workload only (profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timings")
+    ap.add_argument("--only", choices=["square", "decode", "w4a16", "moe", "moe_fp8", "ceilings", "host"],
+                    default=None, help="time one workload only (profiling)")
     ap.add_argument("--no-extra", action="store_true", help="skip the W4A16 and MoE workloads")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the sustained replay with clock sampling")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -171,20 +434,26 @@ def main():
 
     g = qg.Gemm()
     ws = qg.workspace()
+    dev = False if args.no_clocks else _sysfs_device()
+    only = args.only
+    cpu = not args.no_cpu and only is None
+    oracle_cfg = {}
 
     out = {}
     M = N = K = 4096
     flops = 2.0 * M * N * K
-    if args.only in (None, "square"):
+    if only in (None, "square"):
         sq = Workload(g, ws, lambda i: synth.dense_problem(M, N, K, "bf16", "bf16", seed=synth.SEED_A + 10 * i),
                       nsets=4, op=qg.operation())
         kname = sq.runs[0].plan().split()[0].split("=")[1]
-        t = sq.time(args.steps, args.warmup)
+        t = sq.time(args.steps, args.warmup, dev)
         ms_step = t["total_ms"] / args.steps
+        log(f"square {t['kernel_ms_mean'] * 1e3:.1f} us per launch")
         out["square"] = dict(t, kernel=kname, plan=sq.runs[0].plan(), tflops=flops / (ms_step * 1e-3) / 1e12,
                              kernel_tflops=flops / (t["kernel_ms_mean"] * 1e-3) / 1e12)
+        del sq
 
-    if args.only in (None, "decode"):
+    if only in (None, "decode"):
         dec_bytes = 16 * 14336 * 2 + 4096 * 14336 * 2 + 2 * 16 * 4096 * 2
         res = {}
         for name, op in [("splitk8", qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)),
@@ -193,49 +462,73 @@ def main():
             dw = Workload(g, ws, lambda i: synth.dense_problem(16, 4096, 14336, "bf16", "bf16", c_dtype="bf16",
                                                                alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02,
                                                                seed=synth.SEED_A + 10 * i), nsets=3, op=op)
-            t = dw.time(max(20, args.steps // 2), max(5, args.warmup // 2))
+            t = dw.time(max(20, args.steps // 2), max(5, args.warmup // 2), dev)
             res[name] = dict(kernel_us_mean=t["kernel_ms_mean"] * 1e3,
                              gbs=dec_bytes / (t["kernel_ms_mean"] * 1e-3) / 1e9,
                              frac_hbm=dec_bytes / (t["kernel_ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             plan=dw.runs[0].plan(op))
+                             plan=dw.runs[0].plan(op), clocks=t.get("clocks"),
+                             kernel=dw.runs[0].plan(op).split()[0].split("=")[1])
+            log(f"decode {name} {t['kernel_ms_mean'] * 1e3:.2f} us per launch")
+            if cpu and name == "splitk8":
+                oracle_cfg["decode_16x4096x14336_bf16"] = oracle_rows_time(dw.runs[0].p)
             del dw
         out["decode"] = dict(bytes_per_call=dec_bytes, **res)
 
-    extra = not args.no_extra and args.only is None
-    if extra or args.only == "w4a16":
+    extra = not args.no_extra and only is None
+    if extra or only == "w4a16":
         # B 33.5 MB + scales 1 MB per set: 9 sets exceed the 256 MB Infinity Cache
         w4_bytes = 64 * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 64 * 2 + 64 * 8192 * 2
         ww = Workload(g, ws, lambda i: synth.config_w4a16(), nsets=9, op=None, same_data=True)
-        t = ww.time(args.steps, args.warmup)
+        t = ww.time(args.steps, args.warmup, dev)
         us = t["kernel_ms_mean"] * 1e3
+        log(f"w4a16 {us:.2f} us per launch")
         out["w4a16"] = {"kernel_us_mean": round(us, 3), "GB/s": round(w4_bytes / (us * 1e-6) / 1e9, 1),
                         "frac_hbm": round(w4_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                         "TFLOP/s": round(2.0 * 64 * 8192 * 8192 / (us * 1e-6) / 1e12, 2),
-                        "bytes_per_call": w4_bytes, "plan": ww.runs[0].plan()}
+                        "bytes_per_call": w4_bytes, "plan": ww.runs[0].plan(), "clocks": t.get("clocks")}
+        kn = ww.runs[0].plan().split()[0].split("=")[1]
+        out["w4a16"]["traffic"] = traffic_from_profile(kn, "w4a16_64x8192x8192")
+        if cpu:
+            oracle_cfg["w4a16_64x8192x8192"] = oracle_rows_time(ww.runs[0].p)
         del ww
     for fp8 in (False, True):
         name = "moe_fp8" if fp8 else "moe"
-        if not (extra or args.only == name):
+        if not (extra or only == name):
             continue
         # one set of 2.8 GB (bf16) / 1.4 GB (fp8) is far beyond every cache
         mw = Workload(g, ws, lambda i: synth.config_moe(fp8=fp8), nsets=1, op=None)
         p0 = mw.runs[0].p
         mflops = 2.0 * p0["M"] * p0["N"] * p0["K"]
-        t = mw.time(max(10, args.steps // 5), max(3, args.warmup // 5))
+        t = mw.time(max(10, args.steps // 5), max(3, args.warmup // 5), dev)
         us = t["kernel_ms_mean"] * 1e3
+        log(f"{name} {us:.1f} us per launch")
         peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
         out[name] = {"kernel_us_mean": round(us, 1), "TFLOP/s": round(mflops / (us * 1e-6) / 1e12, 1),
                      "frac_peak": round(mflops / (us * 1e-6) / 1e12 / peak, 4), "peak": peak,
-                     "flops_per_call": mflops, "plan": mw.runs[0].plan()}
-        del mw, p0
+                     "flops_per_call": mflops, "plan": mw.runs[0].plan(), "clocks": t.get("clocks")}
+        del mw
+        if cpu:
+            oracle_cfg[f"{name}_64x2048x7168"] = oracle_rows_time(p0, 256)
+        del p0
 
-    if args.only:
+    if only in (None, "ceilings"):
+        out["ceilings"] = {"mfma_bf16": ceiling_mfma(dev)}
+        log(f"mfma ceiling {out['ceilings']['mfma_bf16']['tflops']} TFLOP/s")
+        out["ceilings"]["stream_read"] = ceiling_stream(dev, 4096 * 14336 * 2)
+        log(f"stream ceiling {out['ceilings']['stream_read']['GB/s']} GB/s")
+    if only in (None, "host"):
+        out["host_us_per_call"] = host_timing(g, ws)
+        log(f"host {out['host_us_per_call']}")
+
+    if only:
         print(json.dumps(out))
         return 0
 
     sq_ = out["square"]
     ms_step = sq_["total_ms"] / args.steps
     achieved = sq_["kernel_tflops"]
+    mf = out["ceilings"]["mfma_bf16"]
+    stream = out["ceilings"]["stream_read"]
     line = {
         "metric": "TFLOP/s (% of bf16 MFMA peak) at 4096^3; HBM GB/s at M=16 decode GEMM",
         "value": round(sq_["tflops"], 2),
@@ -255,20 +548,31 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": sq_["kernel"],
                      "kernel_us_mean": round(sq_["kernel_ms_mean"] * 1e3, 3),
-                     "traffic": traffic_from_profile(sq_["kernel"], "square_4096_bf16")},
+                     "traffic": traffic_from_profile(sq_["kernel"], "square_4096_bf16"),
+                     "frac_of_sustained": round(achieved / mf["tflops"], 4),
+                     "sustained_ceiling": "ceilings.mfma_bf16.tflops (MFMA-only loop, same process)"},
+        "clocks": sq_.get("clocks"),
+        "ceilings": out["ceilings"],
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in out["decode"].items()
                    if not isinstance(v, dict)},
     }
     for k in ("splitk8", "streamk"):
         d = out["decode"][k]
         line["decode"][k] = {"kernel_us_mean": round(d["kernel_us_mean"], 3), "GB/s": round(d["gbs"], 1),
-                             "frac_hbm": round(d["frac_hbm"], 4), "plan": d["plan"]}
+                             "frac_hbm": round(d["frac_hbm"], 4),
+                             "frac_of_stream": round(d["gbs"] / stream["GB/s"], 4),
+                             "traffic": traffic_from_profile(d["kernel"], f"decode_16x4096x14336_{k}"),
+                             "plan": d["plan"], "clocks": d["clocks"]}
     for k in ("w4a16", "moe", "moe_fp8"):
         if k in out:
             line[k] = out[k]
+    line["host_us_per_call"] = out["host_us_per_call"]
     if not args.no_cpu:
         p = synth.config_square("bf16")
-        line["cpu_baseline"] = cpu_baseline(p, 2.0 * N * K)
+        line["cpu_baseline"], sample = cpu_baseline(p, 2.0 * N * K)
+        log("cpu baseline done")
+        del p
+        line["cpu_oracle"] = oracle_timings({"square_4096^3_bf16": sample, **oracle_cfg})
     print(json.dumps(line))
     return 0
 

@@ -81,6 +81,8 @@ def lib():
             f.argtypes = [at]
             f.restype = ctypes.c_double
         L.or_num_threads.restype = ctypes.c_int
+        L.or_set_num_threads.argtypes = [ctypes.c_int]
+        L.or_set_num_threads.restype = None
         L.or_quant_codes.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.or_quant_codes.restype = ctypes.c_int
@@ -90,6 +92,11 @@ def lib():
 
 def num_threads() -> int:
     return int(lib().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls from this thread."""
+    lib().or_set_num_threads(int(n))
 
 
 def dec_bf16(bits: int) -> float:

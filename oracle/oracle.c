@@ -238,3 +238,14 @@ int or_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads of later calls made from the calling
+ * thread (n >= 1); used to time the oracle single-threaded. */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

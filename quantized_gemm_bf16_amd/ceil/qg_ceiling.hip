@@ -1,0 +1,134 @@
+// Measurement kernels and host loops of libqgceil.so (see include/qgceil.h):
+// the chip's sustained MFMA rate and shader clock, its sustained streaming
+// read rate, and the host cost of a launch, measured in the benchmark's own
+// process next to the GEMM kernels they bound.
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+
+#include "../../include/qgceil.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaThreads = 512;
+constexpr int kMfmaLds = 96 * 1024;  // > 80 KiB: one workgroup per CU
+constexpr int kStreamThreads = 256;
+constexpr int kStreamLoads = 8;      // 16-byte loads in flight per thread
+
+__global__ __launch_bounds__(kMfmaThreads) void mfma_loop(int iters, float* sink, uint64_t* clk) {
+  __shared__ char lds[kMfmaLds];
+  const int t = threadIdx.x;
+  // operands that depend on the thread, so the loop cannot be folded
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)((float)((t + j) & 7) * 0.125f);
+    b[j] = (__bf16)((float)((t * 3 + j) & 7) * -0.0625f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  if (t == 0) ((volatile char*)lds)[blockIdx.x % kMfmaLds] = 1;  // keeps the LDS allocation
+  __syncthreads();
+  const uint64_t t0 = __builtin_readcyclecounter();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  const uint64_t t1 = __builtin_readcyclecounter();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if (t == 0) {
+    sink[blockIdx.x] = s + (float)((volatile char*)lds)[blockIdx.x % kMfmaLds];
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// Workgroup g reads the 32 KiB blocks g, g + grid, ... : each thread loads
+// kStreamLoads 16-byte pieces 4 KiB apart, all lanes together whole 4 KiB
+// spans, and folds them into one dword. Buffer loads past `bytes` return
+// zero, so the tail needs no branch.
+__global__ __launch_bounds__(kStreamThreads) void stream_read(const char* src, uint32_t bytes, uint32_t* sink) {
+  constexpr uint32_t kBlockBytes = kStreamThreads * kStreamLoads * 16;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, (int)bytes, 0x00020000);
+  i32x4 acc = {0, 0, 0, 0};
+  for (uint64_t off = (uint64_t)blockIdx.x * kBlockBytes; off < bytes; off += (uint64_t)gridDim.x * kBlockBytes) {
+    i32x4 v[kStreamLoads];
+#pragma unroll
+    for (int j = 0; j < kStreamLoads; ++j)
+      v[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, (uint32_t)off + (uint32_t)(j * kStreamThreads + threadIdx.x) * 16, 0, 0));
+#pragma unroll
+    for (int j = 0; j < kStreamLoads; ++j) acc ^= v[j];
+  }
+  sink[(size_t)blockIdx.x * kStreamThreads + threadIdx.x] = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+__global__ void empty_kernel() {}
+
+int launched() {
+  if (hipGetLastError() != hipSuccess) return QG_ERR_HIP;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgc_mfma_loop(int grid, int iters, float* sink, uint64_t* clk, hipStream_t stream) {
+  if (grid < 1 || grid > 65535 || iters < 1 || iters > (1 << 20) || !sink || !clk) return QG_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(kMfmaThreads), 0, stream, iters, sink, clk);
+  return launched();
+}
+
+int qgc_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || bytes >= (size_t(1) << 31) ||
+      (reinterpret_cast<uintptr_t>(src) & 15) || grid < 1 || grid > 65535)
+    return QG_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(kStreamThreads), 0, stream, (const char*)src, (uint32_t)bytes,
+                     sink);
+  return launched();
+}
+
+int qgc_empty(hipStream_t stream) {
+  hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+  return launched();
+}
+
+int qgc_host_us_per_call(qgc_run_fn fn, int n, qg_handle* h, const qg_operation* op, float alpha, const void* A,
+                         const qg_layout* Adesc, const void* U, const qg_layout* Udesc, const void* B,
+                         const qg_layout* Bdesc, const void* V, const qg_layout* Vdesc, float beta, const void* C,
+                         const qg_layout* Cdesc, void* D, const qg_layout* Ddesc, const qg_workspace* ws,
+                         hipStream_t stream, double* us_per_call) {
+  if (!fn || n < 1 || !us_per_call) return QG_ERR_INVALID_ARG;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < n; ++i) {
+    const int st = fn(h, op, alpha, A, Adesc, U, Udesc, B, Bdesc, V, Vdesc, beta, C, Cdesc, D, Ddesc, ws, stream);
+    if (st != QG_OK) return st;
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  *us_per_call = std::chrono::duration<double, std::micro>(t1 - t0).count() / n;
+  return QG_OK;
+}
+
+int qgc_host_us_per_empty(int n, hipStream_t stream, double* us_per_call) {
+  if (n < 1 || !us_per_call) return QG_ERR_INVALID_ARG;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < n; ++i) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  if (hipGetLastError() != hipSuccess) return QG_ERR_HIP;
+  *us_per_call = std::chrono::duration<double, std::micro>(t1 - t0).count() / n;
+  return QG_OK;
+}
+
+}  // extern "C"

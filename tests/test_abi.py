@@ -31,6 +31,33 @@ def test_every_declared_function_is_exported():
     assert set(names) == set(qg.EXPORTS)
 
 
+def test_measurement_library_exports_its_header():
+    from quantized_gemm_bf16_amd import ceiling
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qgceil.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qgc_[a-z_]+)\s*\(", text)))
+    lib = ctypes.CDLL(ceiling.CEIL_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ceiling.EXPORTS)
+
+
+def test_measurement_library_rejects_bad_arguments():
+    # every rejection happens before a launch
+    from quantized_gemm_bf16_amd import ceiling
+    L = ceiling.lib
+    assert L.qgc_mfma_loop(0, 1, FAKE, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_mfma_loop(1, 0, FAKE, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_mfma_loop(1, 1, None, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_stream_read(FAKE, 15, 1, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_stream_read(FAKE + 4, 16, 1, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_stream_read(FAKE, 1 << 31, 1, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_stream_read(FAKE, 16, 65536, FAKE, None) == qg.ERR_INVALID_ARG
+    out = ctypes.c_double()
+    assert L.qgc_host_us_per_empty(0, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
+    assert L.qgc_host_us_per_call(None, 1, None, None, 0.0, None, None, None, None, None, None, None, None, 0.0,
+                                  None, None, None, None, None, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
+
+
 def test_constants_and_strings():
     assert qg.barriers_size() == 1 << 20
     assert qg.partials_size() == 32 << 20
