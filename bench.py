@@ -322,11 +322,18 @@ def host_timing(g, ws, n=500):
     if st == qg.OK:
         out["cache_hit"] = per_call(qg.operation(policy=qg.POLICY_REUSE))
     out["force"] = per_call(qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8))
-    xs = []
-    for _ in range(3):
-        xs.append(qc.host_us_per_empty(n))
-        torch.cuda.synchronize()
-    out["empty_kernel_launch"] = round(statistics.median(xs), 3)
+    # M = 0: qg_run validates the call and returns before planning or launching
+    Ad0, Cd0, Dd0 = (qg.layout("bf16", 0, 14336), qg.layout("bf16", 0, 4096, ld=r.ldn),
+                     qg.layout("bf16", 0, 4096, ld=r.ldn))
+    out["validate_only_m0"] = round(statistics.median(
+        qc.host_us_per_run(n, g, qg.operation(), 1.0, r.A, Ad0, None, None, r.B, r.Bd, None, None, 1.0, r.C, Cd0,
+                           r.D, Dd0, ws.desc) for _ in range(3)), 3)
+    for key, nb in (("empty_kernel_launch", 0), ("empty_kernel_256B_args_launch", 256)):
+        xs = []
+        for _ in range(3):
+            xs.append(qc.host_us_per_empty(n, nb))
+            torch.cuda.synchronize()
+        out[key] = round(statistics.median(xs), 3)
     out["calls_per_loop"] = n
     out["problem"] = "decode M=16 N=4096 K=14336 bf16, C bf16, beta 1"
     return out

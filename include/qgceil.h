@@ -7,7 +7,8 @@
  *   - an MFMA-only loop at the GEMM kernels' occupancy (the sustained matrix
  *     rate, and the shader clock it ran at);
  *   - a streaming read (the sustained HBM read rate);
- *   - an empty kernel (the runtime's launch cost);
+ *   - empty kernels (the runtime's launch cost, without and with a kernel
+ *     argument block);
  *   - a host loop that times calls of a qg_run-shaped function.
  *
  * The DeepGEMM write-up (section 5.2) bases tuning on profiler evidence of
@@ -73,8 +74,12 @@ int qgc_host_us_per_call(qgc_run_fn fn, int n, qg_handle* h, const qg_operation*
                          const qg_layout* Cdesc, void* D, const qg_layout* Ddesc, const qg_workspace* ws,
                          hipStream_t stream, double* us_per_call);
 
-/* Host time of `n` back-to-back qgc_empty launches, microseconds per launch. */
-int qgc_host_us_per_empty(int n, hipStream_t stream, double* us_per_call);
+/* Host time of `n` back-to-back launches of an empty kernel (one workgroup
+ * of 64 threads), microseconds per launch. arg_bytes 0: a kernel without
+ * arguments; 256: one with a 256-byte argument block, which the runtime
+ * copies on every launch (the GEMM kernels take one block of about that
+ * size). Other values are rejected. */
+int qgc_host_us_per_empty(int n, int arg_bytes, hipStream_t stream, double* us_per_call);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,14 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read(const char* src, u
 
 __global__ void empty_kernel() {}
 
+// An empty kernel with a 256-byte argument block: the runtime copies the
+// arguments of every launch, so this is the launch floor for a kernel that
+// takes arguments (the GEMM kernels take one block of about that size).
+struct ArgBlock {
+  char bytes[256];
+};
+__global__ void empty_args_kernel(const ArgBlock) {}
+
 int launched() {
   if (hipGetLastError() != hipSuccess) return QG_ERR_HIP;
   return QG_OK;
@@ -119,11 +127,14 @@ int qgc_host_us_per_call(qgc_run_fn fn, int n, qg_handle* h, const qg_operation*
   return QG_OK;
 }
 
-int qgc_host_us_per_empty(int n, hipStream_t stream, double* us_per_call) {
-  if (n < 1 || !us_per_call) return QG_ERR_INVALID_ARG;
+int qgc_host_us_per_empty(int n, int arg_bytes, hipStream_t stream, double* us_per_call) {
+  if (n < 1 || !us_per_call || !(arg_bytes == 0 || arg_bytes == (int)sizeof(ArgBlock))) return QG_ERR_INVALID_ARG;
+  ArgBlock blk = {};
   const auto t0 = std::chrono::steady_clock::now();
-  for (int i = 0; i < n; ++i) {
-    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+  if (arg_bytes == 0) {
+    for (int i = 0; i < n; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+  } else {
+    for (int i = 0; i < n; ++i) hipLaunchKernelGGL(empty_args_kernel, dim3(1), dim3(64), 0, stream, blk);
   }
   const auto t1 = std::chrono::steady_clock::now();
   if (hipGetLastError() != hipSuccess) return QG_ERR_HIP;

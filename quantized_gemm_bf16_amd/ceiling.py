@@ -30,7 +30,7 @@ def _load():
     L.qgc_host_us_per_call.argtypes = [vp, i32, vp, P(Operation), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp,
                                        P(Layout), vp, P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout),
                                        P(Workspace), vp, P(ctypes.c_double)]
-    L.qgc_host_us_per_empty.argtypes = [i32, vp, P(ctypes.c_double)]
+    L.qgc_host_us_per_empty.argtypes = [i32, i32, vp, P(ctypes.c_double)]
     for n in EXPORTS:
         getattr(L, n).restype = i32
     return L
@@ -67,7 +67,9 @@ def host_us_per_run(n, gemm, op, alpha, A, Ad, U, Ud, B, Bd, V, Vd, beta, C, Cd,
     return out.value
 
 
-def host_us_per_empty(n, stream=None):
+def host_us_per_empty(n, arg_bytes=0, stream=None):
+    """Host microseconds per launch of an empty kernel (arg_bytes 0 or 256)."""
     out = ctypes.c_double()
-    _ok(lib.qgc_host_us_per_empty(n, stream or _current_stream(), ctypes.byref(out)), "qgc_host_us_per_empty")
+    _ok(lib.qgc_host_us_per_empty(n, arg_bytes, stream or _current_stream(), ctypes.byref(out)),
+        "qgc_host_us_per_empty")
     return out.value

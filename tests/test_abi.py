@@ -53,7 +53,8 @@ def test_measurement_library_rejects_bad_arguments():
     assert L.qgc_stream_read(FAKE, 1 << 31, 1, FAKE, None) == qg.ERR_INVALID_ARG
     assert L.qgc_stream_read(FAKE, 16, 65536, FAKE, None) == qg.ERR_INVALID_ARG
     out = ctypes.c_double()
-    assert L.qgc_host_us_per_empty(0, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
+    assert L.qgc_host_us_per_empty(0, 0, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
+    assert L.qgc_host_us_per_empty(1, 8, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
     assert L.qgc_host_us_per_call(None, 1, None, None, 0.0, None, None, None, None, None, None, None, None, 0.0,
                                   None, None, None, None, None, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
 

@@ -63,4 +63,5 @@ def test_host_loops(qc):
     torch.cuda.synchronize()
     assert 0 < us < 10000
     assert 0 < qc.host_us_per_empty(10) < 10000
+    assert 0 < qc.host_us_per_empty(10, 256) < 10000
     torch.cuda.synchronize()
