@@ -165,6 +165,10 @@ int check_layout(const qg_layout* L, bool need_rows_cols_ok = true) {
   if (L->order != QG_ROW_MAJOR) return L->order == QG_COL_MAJOR ? QG_ERR_UNSUPPORTED : QG_ERR_INVALID_ARG;
   if (L->type < 0 || L->type > QG_U4) return QG_ERR_INVALID_ARG;
   if (need_rows_cols_ok && (L->rows < 0 || L->cols < 0)) return QG_ERR_INVALID_ARG;
+  if (L->ld < 0) return QG_ERR_INVALID_ARG;
+  // the kernels index rows, columns and pitches in 32 bits; bounding them
+  // here also keeps the size arithmetic of the checks below from overflowing
+  if (L->rows > INT32_MAX || L->cols > INT32_MAX || L->ld > INT32_MAX) return QG_ERR_UNSUPPORTED;
   return QG_OK;
 }
 
@@ -931,7 +935,7 @@ int qg_export(qg_handle* h, char* buf, size_t cap, size_t* len) {
     for (auto& kv : h->cache) {
       const Entry& e = kv.second;
       char line[256];
-      snprintf(line, sizeof line, " kernel=%s schedule=%s split=%d programs=%d us=%.3f\n", kKernels[e.c.kernel].name,
+      snprintf(line, sizeof line, " kernel=%s schedule=%s split=%d programs=%d us=%.9g\n", kKernels[e.c.kernel].name,
                sched_name(e.c.mode), e.c.split, e.c.programs, e.us);
       os << kv.first << line;
     }
@@ -981,6 +985,7 @@ int qg_import(qg_handle* h, const char* buf, size_t len) {
       e.us = strtod(uk.c_str() + 3, &end);
       if (*end) return QG_ERR_FORMAT;
       if (e.c.kernel < 0 || e.c.mode < 0 || e.c.split < 1 || e.c.programs < 0) return QG_ERR_FORMAT;
+      if (!std::isfinite(e.us) || e.us < 0) return QG_ERR_FORMAT;
       staged[key] = e;
       ++got;
     }

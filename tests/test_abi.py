@@ -279,8 +279,8 @@ def test_tuning_sequence(g):
 
 
 CACHE = """qgemm-cache 2 arch=gfx950 entries=2
-16|bf16.bf16.-.bf16.q00.e0.x0.n4096.k14336 kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4 programs=0 us=20.500
-4096|bf16.bf16.-.bf16.q00.e0.x0.n4096.k4096 kernel=tile_BF16_128x128x128b_w2x2_s4 schedule=dp split=1 programs=0 us=90.000
+16|bf16.bf16.-.bf16.q00.e0.x0.n4096.k14336 kernel=tile_BF16_32x64x128b_w1x2_s6 schedule=splitk split=4 programs=0 us=20.5
+4096|bf16.bf16.-.bf16.q00.e0.x0.n4096.k4096 kernel=tile_BF16_128x128x128b_w2x2_s4 schedule=dp split=1 programs=0 us=90
 """
 
 
@@ -315,7 +315,10 @@ def test_cache_import_export_roundtrip_and_lookup():
     CACHE.replace("kernel=tile_BF16_32x64x128b_w1x2_s6", "kernel=no_such_kernel"),
     CACHE.replace("schedule=dp", "schedule=zigzag"),
     CACHE.replace("split=4", "split=x"),
-    CACHE.replace("us=90.000", "us=90.000 extra"),
+    CACHE.replace("us=90", "us=90 extra"),
+    CACHE.replace("us=90", "us=-90"),
+    CACHE.replace("us=90", "us=nan"),
+    CACHE.replace("us=90", "us=inf"),
     CACHE[: len(CACHE) // 2],
 ])
 def test_cache_import_is_all_or_nothing(bad):
