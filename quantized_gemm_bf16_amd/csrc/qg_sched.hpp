@@ -203,14 +203,35 @@ struct Sched {
   __device__ __forceinline__ static void run_grouped(const Args& a, char* smem, int* pref) {
     const bool batched = a.offsets == nullptr;
     if (!batched) {
-      // pref[0..E] = prefix of ceil(rows_e / BM); E <= 1023 (host checked)
-      if (threadIdx.x == 0) {
-        int acc = 0;
-        pref[0] = 0;
-        for (int e = 0; e < a.E; ++e) {
-          const int rows = a.offsets[e + 1] - a.offsets[e];
-          acc += rows > 0 ? (rows + Core::BM - 1) / Core::BM : 0;
-          pref[e + 1] = acc;
+      // pref[0..E] = prefix of ceil(rows_e / BM), E <= 1023 (host checked),
+      // built by the first wave: lane l takes experts [16 l, 16 l + 16) (its
+      // 17 offsets load together), sums them, and a wave-wide scan of the
+      // lane sums gives each lane its starting value.
+      if (threadIdx.x < 64) {
+        constexpr int PER = 16;
+        const int l = threadIdx.x, e0 = l * PER;
+        int cnt[PER], off[PER + 1];
+#pragma unroll
+        for (int j = 0; j <= PER; ++j) off[j] = e0 + j <= a.E ? a.offsets[e0 + j] : 0;
+        int tot = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int rows = e0 + j < a.E ? off[j + 1] - off[j] : 0;
+          cnt[j] = rows > 0 ? (rows + Core::BM - 1) / Core::BM : 0;
+          tot += cnt[j];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d, 64);
+          if (l >= d) incl += y;
+        }
+        int run = incl - tot;
+        if (l == 0) pref[0] = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          run += cnt[j];
+          if (e0 + j < a.E) pref[e0 + j + 1] = run;
         }
       }
       __syncthreads();

@@ -180,6 +180,24 @@ def test_grouped_small_with_empty_experts(g, ws):
         check_against_oracle(p, r.run(op), what=f"grouped {kname}")
 
 
+@pytest.mark.parametrize("E", [1, 16, 17, 1023])
+def test_grouped_expert_counts(g, ws, E):
+    # the per-expert m-tile prefix is built by one wave, 16 experts a lane:
+    # 16 and 17 experts end on and just past a lane's share, 1023 is the most
+    # the engine takes (64 lanes x 16); every third expert is empty
+    rng = np.random.default_rng(E)
+    counts = rng.integers(1, 70, size=E).astype(np.int32)
+    counts[::3] = 0
+    if counts.sum() == 0:
+        counts[-1] = 5
+    p = synth.grouped_problem(counts, 72, 64, seed=E)
+    r = Run(g, p, ws)
+    for kname in ["tile_BF16_32x128x128b_w1x4_s4", "tile_BF16_128x128x128b_w2x2_s4"]:
+        op = qg.operation(policy=qg.POLICY_FORCE, kernel=kidx(kname))
+        print(E, kname, r.plan(op), flush=True)
+        check_against_oracle(p, r.run(op), what=f"grouped E={E} {kname}")
+
+
 def test_tiny_config_plan_is_logged(g, ws):
     p = synth.config_tiny()
     desc = Run(g, p, ws).plan()
