@@ -69,6 +69,16 @@ __device__ __forceinline__ void load_lds_x1a(const i32x4& rsrc, void* lds_wave_b
       : "memory", "m0");
 }
 
+// A copy of a workgroup-uniform value that the compiler cannot move out of
+// the branch it is taken in (an empty volatile asm with the value tied to its
+// output). Code that depends on the copy stays inside a rarely taken branch
+// instead of being hoisted out of the loop around it, where its results
+// would occupy registers (or spill) for the whole loop.
+__device__ __forceinline__ uint32_t pinned(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // Zeroes, in LDS, the bytes of a 16-byte chunk from byte `keep` on
 // (0 < keep < 16). When K * element size is not a multiple of 16, the chunk
 // that holds the end of a row's K elements also holds bytes past K (row

@@ -107,16 +107,17 @@ struct F8 : Tile<Cfg> {
     // loaded for the k-tile that holds K's end (as in the tile core).
     const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / 128) : -1;
     auto trim = [&](int stage, int kt) {
+      const uint32_t kb = pinned(kbytes);  // keeps this work inside the branch
       char* sbase = smem + stage * Cfg::STAGE8;
       const uint32_t kk = (uint32_t)kt * 128;
 #pragma unroll
       for (int i = 0; i < Cfg::LA; ++i) {
-        const int keep = (int)(kbytes - kk - chA[i]);
+        const int keep = (int)(kb - kk - chA[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(sbase + (w * Cfg::LA + i) * 1024 + l * 16, keep);
       }
 #pragma unroll
       for (int i = 0; i < Cfg::LB; ++i) {
-        const int keep = (int)(kbytes - kk - chB[i]);
+        const int keep = (int)(kb - kk - chB[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024 + l * 16, keep);
       }
     };
@@ -186,6 +187,8 @@ struct F8 : Tile<Cfg> {
       if (u.kb + it + 1 == ktail) trim((it + 1) % S, ktail);
       lds_barrier();
       issue(st, u.kb + it + S);
+      // promotion of the k-tile's raw sums (measured: faster here, after the
+      // barrier, than interleaved block by block with the MFMAs)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll

@@ -162,16 +162,17 @@ struct Skinny {
     // landed; the wave's LDS accesses stay in order, so its reads see this).
     const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / Cfg::BLKB) : -1;
     auto trim = [&](int d, int blk) {
+      const uint32_t kb = pinned(kbytes);  // keeps this work inside the branch
       char* base = ring + d * Cfg::SLOT;
       const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
-        const int keep = (int)(kbytes - kk - chB[i]);
+        const int keep = (int)(kb - kk - chB[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(base + i * 1024 + l * 16, keep);
       }
 #pragma unroll
       for (int i = 0; i < LA; ++i) {
-        const int keep = (int)(kbytes - kk - chA[i]);
+        const int keep = (int)(kb - kk - chA[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(base + BNW * Cfg::BLKB + i * 1024 + l * 16, keep);
       }
     };
@@ -313,14 +314,15 @@ struct Skinny {
     // after their own copy has landed, so the last write is a trimmed one.
     const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / Cfg::BLKB) : -1;
     auto trim = [&](int d, int blk) {
+      const uint32_t kb = pinned(kbytes);  // keeps this work inside the branch
       char* base = bring + d * Cfg::SLOT;
       const uint32_t kk = (uint32_t)blk * Cfg::BLKB;
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
-        const int keep = (int)(kbytes - kk - chB[i]);
+        const int keep = (int)(kb - kk - chB[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(base + i * 1024 + l * 16, keep);
       }
-      const int keep = (int)(kbytes - kk - chA);
+      const int keep = (int)(kb - kk - chA);
       if (keep > 0 && keep < 16) lds_chunk_trim(aring + d * Cfg::ASLOT + ia * 1024 + l * 16, keep);
     };
     i32x4 fb[ST][TN], fa[ST][MT];

@@ -326,16 +326,17 @@ struct Tile {
     // bytes past K in the chunks it loaded.
     const int ktail = (kbytes & 15) ? (int)((kbytes - 1) / ROWB) : -1;
     auto trim = [&](int stage, int kt) {
+      const uint32_t kb = pinned(kbytes);  // keeps this work inside the branch
       char* sbase = smem + stage * Cfg::STAGE_BYTES;
       const uint32_t kk = (uint32_t)kt * ROWB;
 #pragma unroll
       for (int i = 0; i < Cfg::LA; ++i) {
-        const int keep = (int)(kbytes - kk - chA[i]);
+        const int keep = (int)(kb - kk - chA[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(sbase + (w * Cfg::LA + i) * 1024 + l * 16, keep);
       }
 #pragma unroll
       for (int i = 0; i < Cfg::LB; ++i) {
-        const int keep = (int)(kbytes - kk - chB[i]);
+        const int keep = (int)(kb - kk - chB[i]);
         if (keep > 0 && keep < 16) lds_chunk_trim(sbase + Cfg::A_BYTES + (w * Cfg::LB + i) * 1024 + l * 16, keep);
       }
     };
