@@ -95,6 +95,14 @@ __device__ __forceinline__ uint32_t opaque_vgpr() {
   return r;
 }
 
+// XOR key of an A row's 16-byte chunks in LDS (512-byte rows): the low four
+// row bits rotated left by one. The fragment reads take one chunk of 16
+// consecutive rows per 16-lane group, the lane groups four chunks apart; with
+// the plain key (row & 15) the LDS bank-conflict counter reads about one
+// conflict cycle per conflict-free cycle for that pattern (a probe of this
+// exact access), with the rotated key none.
+__device__ __forceinline__ int akey(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
 template <class Cfg>
 struct W4 {
   static constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT, TN = Cfg::TN, MT = Cfg::MT;
@@ -133,7 +141,7 @@ struct W4 {
 #pragma unroll
     for (int i = 0; i < Cfg::LA; ++i) {
       const int row = (w * Cfg::LA + i) * Cfg::A_RPI + l / Cfg::A_CPR;
-      chA[i] = (uint32_t)(((l % Cfg::A_CPR) ^ (row & 15)) * 16);
+      chA[i] = (uint32_t)(((l % Cfg::A_CPR) ^ akey(row)) * 16);
       offA[i] = (uint32_t)(row * lda_b) + chA[i];
     }
 #pragma unroll
@@ -242,7 +250,7 @@ struct W4 {
         for (int mt = 0; mt < MT; ++mt) {
           const int row = mt * 16 + orow;
           const int c = wk * 16 + 4 * og + j;
-          af[mt] = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ (row & 15)) << 4));
+          af[mt] = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ akey(row)) << 4));
         }
         if constexpr (ZP) {
 #pragma unroll
@@ -258,7 +266,7 @@ struct W4 {
           const i32x4 bz = {(int)zsym, (int)zsym, (int)zsym, (int)zsym};
           const int row = (wn % MT) * 16 + orow;
           const int c = wk * 16 + 4 * og + j;
-          const i32x4 am = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ (row & 15)) << 4));
+          const i32x4 am = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ akey(row)) << 4));
           Zc = mfma16_bf16(bz, am, Zc);
         }
 #pragma unroll
