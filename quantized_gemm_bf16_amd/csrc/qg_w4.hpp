@@ -31,8 +31,8 @@
 // 256 WK bytes), B rows (BN x 64 WK bytes of nibbles), the scales (one dword
 // per column: WK = 2 fp16) and the zero points (one dword per column) go
 // global -> LDS with direct loads into an S-stage ring. At the end of a unit
-// the WK partial sums are added through LDS in wk order (deterministic), and
-// the wk = 0 waves hold the tile.
+// the two k-group waves of a column group exchange halves through LDS and
+// each keeps half of the group's n-tiles (deterministic: a + b == b + a).
 #pragma once
 #include <type_traits>
 
@@ -390,30 +390,38 @@ struct W4 {
       correct(P, sc, zv);
     }
 
-    // Add the k-group partial sums in wk order into the wk = 0 waves.
+    // Sum the two k-group waves of a column group, splitting the tile: wave
+    // (wn, wk) keeps n-tiles [wk TO, (wk + 1) TO) and hands the other half to
+    // its partner through LDS (a + b == b + a exactly, so the result does
+    // not depend on which wave adds). Both waves then write, read back and
+    // store half of the column group's outputs.
     f32x4* red = (f32x4*)smem;
-    if (wk > 0) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
+    for (int tn = 0; tn < TN; ++tn) {
+      if (tn / TO == wk) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[((((wk - 1) * WN + wn) * TN + tn) * MT + mt) * 64 + l] = acc.v[tn][mt];
+      for (int mt = 0; mt < MT; ++mt) red[((wn * TN + tn) * MT + mt) * 64 + l] = acc.v[tn][mt];
     }
     __syncthreads();
-    if (wk == 0) {
 #pragma unroll
-      for (int k2 = 1; k2 < WK; ++k2)
+    for (int tn = 0; tn < TN; ++tn) {
+      if (tn / TO != wk) continue;
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] += red[((((k2 - 1) * WN + wn) * TN + tn) * MT + mt) * 64 + l];
+      for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] += red[((wn * TN + tn) * MT + mt) * 64 + l];
     }
     __syncthreads();  // the ring is reused by the next unit
   }
 
-  // Lane holds D[m][n .. n+3] with m = 16 mt + l%16, n = n0 + wn*BNW + 16 tn + 4 (l/16).
+  // Lane holds D[m][n .. n+3] with m = 16 mt + l%16, n = n0 + wn*BNW + 16 tn + 4 (l/16),
+  // for the n-tiles tn its k-group wave keeps (see the end of mainloop).
+  static constexpr int TO = TN / WK;  // n-tiles kept per wave
+  static_assert(TO * WK == TN, "the finished tile splits over the k-group waves by n-tiles");
+  // Whether n-tile tn is kept by the calling wave. Register arrays are only
+  // ever indexed with compile-time indices (loops over every tn with this
+  // uniform test): a wave-dependent index would send them to scratch.
+  __device__ __forceinline__ static bool keeps(int tn) { return tn / TO == wk_of(wave_id()); }
   __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* /*smem*/) {
     const int w = wave_id(), l = lane_id();
-    if (wk_of(w) != 0) return;
     const int wn = wn_of(w);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -421,6 +429,7 @@ struct W4 {
       if (m >= u.m_end) continue;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
+        if (!keeps(tn)) continue;
         const int n = u.n0 + wn * BNW + tn * 16 + 4 * (l >> 4);
         if (n < a.N) epi_store4(a, m, n, acc.v[tn][mt]);
       }
@@ -430,25 +439,39 @@ struct W4 {
   __device__ __forceinline__ static __amdgpu_buffer_rsrc_t slot_rsrc(const Args& a, int slot) {
     return make_rsrc((const char*)a.partials + (size_t)slot * (BM * BN * 4), BM * BN * 4);
   }
-  // Partial tile layout: [wn][tn][mt][lane] x 16 bytes (written by the wk = 0 waves).
+  // Partial tile layout: [wn][tn][mt][lane] x 16 bytes (each (wn, tn) written by the wave that keeps it).
   __device__ __forceinline__ static uint32_t pofs(int tn, int mt) {
     return (uint32_t)((((wn_of(wave_id()) * TN + tn) * MT + mt) * 64 + lane_id()) * 16);
   }
   __device__ __forceinline__ static void write_partial(const Args& a, int slot, Acc& acc) {
-    if (wk_of(wave_id()) != 0) return;
     const auto r = slot_rsrc(a, slot);
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+    for (int tn = 0; tn < TN; ++tn) {
+      if (!keeps(tn)) continue;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) store_sc1_x4(r, pofs(tn, mt), __builtin_bit_cast(i32x4, acc.v[tn][mt]));
+    }
   }
-  // Chunk c = tn * MT + mt of a lane's partial tile.
+  // Chunk c = i * MT + mt of a lane's partial tile: the wave's i-th kept
+  // n-tile (wk TO + i), m-tile mt.
   using S4 = f32x4;
-  static constexpr int NCH = TN * MT;
-  __device__ __forceinline__ static bool holds_partial() { return wk_of(wave_id()) == 0; }
-  __device__ __forceinline__ static uint32_t chunk_off(int c) { return pofs(c / MT, c % MT); }
-  __device__ __forceinline__ static S4 get4(const Acc& acc, int c) { return acc.v[c / MT][c % MT]; }
-  __device__ __forceinline__ static void set4(Acc& acc, int c, const S4& x) { acc.v[c / MT][c % MT] = x; }
+  static constexpr int NCH = TO * MT;
+  __device__ __forceinline__ static bool holds_partial() { return true; }
+  __device__ __forceinline__ static uint32_t chunk_off(int c) {
+    return pofs(wk_of(wave_id()) * TO + c / MT, c % MT);
+  }
+  __device__ __forceinline__ static S4 get4(const Acc& acc, int c) {
+    S4 x = acc.v[c / MT][c % MT];
+#pragma unroll
+    for (int tn = TO; tn < TN; ++tn)
+      if (tn / TO == wk_of(wave_id()) && tn % TO == c / MT) x = acc.v[tn][c % MT];
+    return x;
+  }
+  __device__ __forceinline__ static void set4(Acc& acc, int c, const S4& x) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      if (tn / TO == wk_of(wave_id()) && tn % TO == c / MT) acc.v[tn][c % MT] = x;
+  }
 };
 
 template <class Cfg>
