@@ -1,4 +1,4 @@
-// Host-side driver of libqgemm's C ABI for AddressSanitizer /
+// Host-side exerciser of libqgemm's C ABI for AddressSanitizer /
 // UndefinedBehaviorSanitizer builds (host code instrumented, GPU code not).
 // It runs on a machine without a GPU: the handle is then offline, so every
 // qg_run stops at validation or before its launch, while planning, the
@@ -352,7 +352,7 @@ int main() {
   // placeholder addresses
   int devices = 0;
   if (hipGetDeviceCount(&devices) == hipSuccess && devices > 0) {
-    std::printf("abi_asan: a GPU is visible; this driver only runs without one\n");
+    std::printf("abi_asan: a GPU is visible; this program only runs without one\n");
     return 77;
   }
   qg_handle* h = nullptr;

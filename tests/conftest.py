@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 def pytest_sessionstart(session):
     # The C-ABI library and the oracle are built in-tree; build them if absent
-    # (the GPU machine receives them prebuilt).
+    # (a machine that only runs the tests receives them prebuilt).
     lib = os.path.join(ROOT, "quantized_gemm_bf16_amd", "libqgemm.so")
     if not os.path.exists(lib):
         # loaded by path: the package's own import needs the library

@@ -60,7 +60,7 @@ def test_c_abi_under_host_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=600)
     out = r.stdout + r.stderr
     if r.returncode == 77:
-        pytest.skip("a GPU is visible to the driver")
+        pytest.skip("a GPU is visible to the test program")
     assert r.returncode == 0 and "abi_asan: ok" in out, out[-4000:]
     assert "ERROR: AddressSanitizer" not in out and "runtime error:" not in out, out[-4000:]
 
