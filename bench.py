@@ -475,7 +475,7 @@ def main():
             dw = Workload(g, ws, lambda i: synth.dense_problem(16, 4096, 14336, "bf16", "bf16", c_dtype="bf16",
                                                                alpha=1.0, beta=1.0, a_std=0.02, b_std=0.02,
                                                                seed=synth.SEED_A + 10 * i), nsets=3, op=op)
-            t = dw.time(max(20, args.steps // 2), max(5, args.warmup // 2), dev)
+            t = dw.time(max(20, args.steps), max(5, args.warmup), dev)
             res[name] = dict(kernel_us_mean=t["kernel_ms_mean"] * 1e3,
                              gbs=dec_bytes / (t["kernel_ms_mean"] * 1e-3) / 1e9,
                              frac_hbm=dec_bytes / (t["kernel_ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -115,9 +115,23 @@ struct W4 {
   __device__ __forceinline__ static int wn_of(int w) { return w % WN; }
   __device__ __forceinline__ static int wk_of(int w) { return w / WN; }
 
+  // The k-group of a wave is a compile-time constant in each of two copies
+  // of the loop (a uniform branch picks one per wave): the half of a scale
+  // dword that the group uses, the swizzled chunk offsets and the tile split
+  // at the end then cost no instructions in the loop.
   __device__ __forceinline__ static void mainloop(const Args& a, const Unit& u, char* smem, Acc& acc) {
+    if (wk_of(wave_id()) == 0)
+      mainloop_k(std::integral_constant<int, 0>{}, a, u, smem, acc);
+    else
+      mainloop_k(std::integral_constant<int, 1>{}, a, u, smem, acc);
+  }
+
+  template <int WKC>
+  __device__ __forceinline__ static void mainloop_k(std::integral_constant<int, WKC>, const Args& a, const Unit& u,
+                                                    char* smem, Acc& acc) {
     const int w = wave_id(), l = lane_id();
-    const int wn = wn_of(w), wk = wk_of(w);
+    const int wn = wn_of(w);
+    constexpr int wk = WKC;
     const int64_t lda_b = a.lda * 2, ldb_b = a.ldb * 4, ldv_b = a.ldv * 2;
     const uint32_t abytes = (uint32_t)a.K * 2, bbytes = (uint32_t)a.K / 2;  // valid bytes of an A / B row
     const int groups = a.K / Cfg::GK;
@@ -182,6 +196,29 @@ struct W4 {
     };
 
     const int orow = l & 15, og = l >> 4;
+    // Per-lane LDS offsets of the fragments inside a ring stage, fixed for
+    // the whole loop. The swizzle keys depend on the low row bits only, so
+    // the m-tile (A) and n-tile (B, scales) parts are whole multiples of 16
+    // rows and enter the reads as immediate offsets. A step adds the stage
+    // base to each of these once (rebase) and reads at immediate offsets
+    // from the result.
+    uint32_t lA[4];  // A rows orow of m-tile 0, k chunk 16 wk + 4 og + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lA[j] = (uint32_t)(orow * Cfg::A_ROWB + (((wk * 16 + 4 * og + j) ^ akey(orow)) << 4));
+    const uint32_t lZm = (uint32_t)((wn % MT) * 16 * Cfg::A_ROWB);  // m-tile of this wave's Z chain
+    const uint32_t lB = (uint32_t)(Cfg::A_BYTES + (wn * BNW + orow) * Cfg::B_ROWB +
+                                     (((wk * 4 + og) ^ ((orow >> 1) & 7)) << 4));
+    const uint32_t lS = (uint32_t)(Cfg::A_BYTES + Cfg::B_BYTES + (wn * BNW + 4 * og) * 4);
+    const uint32_t lZ = (uint32_t)(Cfg::A_BYTES + Cfg::B_BYTES + Cfg::S_BYTES + (wn * BNW + orow) * 4);
+    static_assert(BNW % 16 == 0, "n-tiles keep the B swizzle key");
+    // stage base + per-lane offset as a value the compiler cannot split
+    // again: without this it keeps one register per (m-tile, k-step) address
+    // and adds the stage to each of them before every read
+    auto rebase = [](uint32_t stage_base, uint32_t off) {
+      uint32_t x = stage_base + off;
+      asm volatile("" : "+v"(x));
+      return x;
+    };
     const uint32_t c128 = opaque_vgpr<0x43004300u>(), m4 = opaque_sgpr<0x000F000Fu>();
     // byte permutes: dword r = [byte r of w, 0, byte r of (w >> 4), 0]
     constexpr uint32_t kSel0 = 0x0C040C00u, kSel1 = 0x0C050C01u, kSel2 = 0x0C060C02u, kSel3 = 0x0C070C03u;
@@ -200,35 +237,37 @@ struct W4 {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc.v[tn][mt] = f32x4{};
 
+    // The scale of a group: half wk of the dword holding the k-tile's two
+    // fp16 scales (a conversion the FMAs that use it absorb).
+    auto scale = [](uint32_t d) { return f16_bits_to_f32((uint16_t)(wk ? d >> 16 : d)); };
+    // With K / 128 odd, the second group of the last k-tile lies past K: its
+    // P and Z are 0 and its scale slot holds padding (possibly Inf or NaN), so
+    // the lane that loaded the slot writes 0 there once its load has landed,
+    // before the barrier that hands the stage to the other waves.
+    const int ztail = role == 0 && (groups & 1) ? groups / 2 : -1;
+    auto scale_tail = [&](int st, int kt) {
+      if (kt == ztail) *(uint16_t*)(dptr + st * dstride + 4 * l + 2) = 0;
+    };
+
     // P (and, with zero points, Z) of group 2 kt + wk of the k-tile in ring
-    // stage st, plus the group's scales of the lane's columns (0 past K).
-    auto group = [&](int st, int kt, auto with_z, f32x4 (&P)[TN][MT], float (&sc)[TN][4], auto&& hook) {
+    // stage st, plus the scale dwords of the lane's columns.
+    auto group = [&](int st, int kt, auto with_z, f32x4 (&P)[TN][MT], uint32_t (&sc)[TN][4], auto&& hook) {
       constexpr bool ZP = decltype(with_z)::value;
-      const char* sA = smem + st * Cfg::STAGE;
-      const char* sB = sA + Cfg::A_BYTES;
-      const uint32_t* sS = (const uint32_t*)(sB + Cfg::B_BYTES);
-      const uint32_t* sZ = (const uint32_t*)((const char*)sS + Cfg::S_BYTES);
+      const uint32_t sbase = (uint32_t)(st * Cfg::STAGE);
       const int g = 2 * kt + wk;
       // B words of this lane: row orow of each n-tile, the group's 16-byte
       // chunk og (4 words, one per k-step)
       i32x4 bw[TN];
+      const uint32_t bB = rebase(sbase, lB);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) bw[tn] = *(const i32x4*)(smem + bB + tn * 16 * Cfg::B_ROWB);
+      // scale dwords of the lane's output columns n = 4 og + r
+      const uint32_t bS = rebase(sbase, lS);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int row = wn * BNW + tn * 16 + orow;
-        const int c = wk * 4 + og;
-        bw[tn] = *(const i32x4*)(sB + row * Cfg::B_ROWB + ((c ^ ((row >> 1) & 7)) << 4));
-      }
-      // scales of the lane's output columns n = 4 og + r; a group past K (the
-      // second of a k-tile when K / 128 is odd) has P = Z = 0 and its scale
-      // slot may hold padding, so its scale is 0 (the dwords are always read
-      // and masked as bits: no branch and wait around each LDS read)
-      const uint32_t gmask = g < groups ? 0xFFFFu : 0u;
-      const int shift = wk ? 16 : 0;
+        const i32x4 sd = *(const i32x4*)(smem + bS + tn * 16 * 4);
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const i32x4 sd = *(const i32x4*)(sS + wn * BNW + tn * 16 + 4 * og);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[tn][r] = f16_bits_to_f32((uint16_t)(((uint32_t)sd[r] >> shift) & gmask));
+        for (int r = 0; r < 4; ++r) sc[tn][r] = (uint32_t)sd[r];
       }
       // asymmetric: the zero point of the lane's B row (the MFMA's first
       // operand row, i.e. column n)
@@ -236,7 +275,7 @@ struct W4 {
       if constexpr (ZP) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const uint32_t zd = sZ[wn * BNW + tn * 16 + orow];
+          const uint32_t zd = *(const uint32_t*)(smem + rebase(sbase, lZ) + tn * 16 * 4);
           zb[tn] = c128 | (((zd >> (8 * (g & 3))) & 0xFu) * 0x00010001u);
         }
       }
@@ -246,12 +285,9 @@ struct W4 {
       for (int j = 0; j < 4; ++j) {
         // A fragments: k chunk 16 wk + 4 og + j of rows orow of each m-tile
         i32x4 af[MT];
+        const uint32_t bA = rebase(sbase, lA[j]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int row = mt * 16 + orow;
-          const int c = wk * 16 + 4 * og + j;
-          af[mt] = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ akey(row)) << 4));
-        }
+        for (int mt = 0; mt < MT; ++mt) af[mt] = *(const i32x4*)(smem + bA + mt * 16 * Cfg::A_ROWB);
         if constexpr (ZP) {
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
@@ -264,9 +300,7 @@ struct W4 {
           // wave runs the chain so that the loop body has no branch, and the
           // waves with wn < MT publish it
           const i32x4 bz = {(int)zsym, (int)zsym, (int)zsym, (int)zsym};
-          const int row = (wn % MT) * 16 + orow;
-          const int c = wk * 16 + 4 * og + j;
-          const i32x4 am = *(const i32x4*)(sA + row * Cfg::A_ROWB + ((c ^ akey(row)) << 4));
+          const i32x4 am = *(const i32x4*)(smem + bA + lZm);
           Zc = mfma16_bf16(bz, am, Zc);
         }
 #pragma unroll
@@ -291,7 +325,7 @@ struct W4 {
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              acc.v[tn][mt][r] = __builtin_fmaf(sc[tn][r], P[tn][mt][r] - Z[tn][mt][r], acc.v[tn][mt][r]);
+              acc.v[tn][mt][r] = __builtin_fmaf(scale(sc[tn][r]), P[tn][mt][r] - Z[tn][mt][r], acc.v[tn][mt][r]);
       } else {
         // lane (og, orow) holds Z of row orow (every output column of the
         // chain carries the same value); each lane writes its own copy, so
@@ -306,14 +340,14 @@ struct W4 {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) zv[mt] = zr[mt];
     };
-    auto correct_mt = [&](int mt, const f32x4 (&P)[TN][MT], const float (&sc)[TN][4], const float (&zv)[MT]) {
+    auto correct_mt = [&](int mt, const f32x4 (&P)[TN][MT], const uint32_t (&sc)[TN][4], const float (&zv)[MT]) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          acc.v[tn][mt][r] = __builtin_fmaf(sc[tn][r], P[tn][mt][r] - zv[mt], acc.v[tn][mt][r]);
+          acc.v[tn][mt][r] = __builtin_fmaf(scale(sc[tn][r]), P[tn][mt][r] - zv[mt], acc.v[tn][mt][r]);
     };
-    auto correct = [&](const f32x4 (&P)[TN][MT], const float (&sc)[TN][4], const float (&zv)[MT]) {
+    auto correct = [&](const f32x4 (&P)[TN][MT], const uint32_t (&sc)[TN][4], const float (&zv)[MT]) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) correct_mt(mt, P, sc, zv);
     };
@@ -324,10 +358,11 @@ struct W4 {
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) issue(st, u.kb + st);
     f32x4 P[TN][MT];
-    float sc[TN][4];
+    uint32_t sc[TN][4];
     if (has_z) {
       for (int it = 0; it < nk; ++it) {
         wait_vmcnt<Cfg::LPW * (S - 2)>();
+        scale_tail(it % S, u.kb + it);
         lds_barrier();
         issue((it + S - 1) % S, u.kb + it + S - 1);
         group(it % S, u.kb + it, std::true_type{}, P, sc, no_hook);
@@ -340,16 +375,17 @@ struct W4 {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) P[tn][mt] = f32x4{};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[tn][r] = 0.f;
+        for (int r = 0; r < 4; ++r) sc[tn][r] = 0u;
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) zx[zslot(u.kb - 1, wk, og) + orow * MT + mt] = 0.f;
       // one k-tile: correct the previous group (Pq, sq) while computing this
       // one into (Pc, sc_); the loop below alternates two register sets
       // instead of copying them
-      auto step = [&](int it, f32x4 (&Pc)[TN][MT], float (&scc)[TN][4], const f32x4 (&Pq)[TN][MT],
-                      const float (&sq)[TN][4]) {
+      auto step = [&](int it, f32x4 (&Pc)[TN][MT], uint32_t (&scc)[TN][4], const f32x4 (&Pq)[TN][MT],
+                      const uint32_t (&sq)[TN][4]) {
         wait_vmcnt<Cfg::LPW * (S - 2)>();
+        scale_tail(it % S, u.kb + it);
         lds_barrier();
         // the previous group's Z values, read before this group writes the
         // other half of the exchange (the compiler cannot tell them apart)
@@ -365,7 +401,7 @@ struct W4 {
         });
       };
       f32x4 P2[TN][MT];
-      float sc2[TN][4];
+      uint32_t sc2[TN][4];
       int it = 0;
       for (; it + 1 < nk; it += 2) {
         step(it, P2, sc2, P, sc);
