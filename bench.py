@@ -89,13 +89,14 @@ def log(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
-def graph_time(step, steps, warmup):
+def graph_time(step, steps, warmup, warm_ms=100.0):
     """Capture `steps` calls of step(i) in one HIP graph and time one replay
     with HIP events on the launch stream (no host gaps between launches, so
     the per-launch figure is device time). The `warmup` untimed steps run
-    as replays of the same graph queued right before the timed one, so the
-    timed steps start on a busy GPU with a graph that has been replayed
-    before. Returns the timing and the graph (for sustain())."""
+    as replays of the same graph, followed by at least `warm_ms` of replays
+    queued right before the timed one, so the timed steps start on a GPU
+    that has been busy with this graph for a while. Returns the timing and
+    the graph (for sustain())."""
     import torch
     for i in range(min(warmup, 3)):  # eager first calls (code objects, caches)
         step(i)
@@ -110,7 +111,15 @@ def graph_time(step, steps, warmup):
     w0 = time.perf_counter()
     # at least three: the first replays of a freshly captured graph run
     # slower (measured: 115.5 vs 109.3 us per 4096^3 kernel), then it is steady
-    for _ in range(max(3, -(-warmup // steps))):
+    nwarm = max(3, -(-warmup // steps))
+    for _ in range(nwarm):
+        graph.replay()
+    torch.cuda.synchronize()
+    # then at least warm_ms of back-to-back replays right before the timed
+    # one: short kernels timed after a few ms of work read 6-7 % slower than
+    # over a sustained second (clocks and power still settling)
+    per = (time.perf_counter() - w0) * 1e3 / nwarm
+    for _ in range(int(warm_ms / max(per, 1e-3))):
         graph.replay()
     e0.record(stream)
     graph.replay()
