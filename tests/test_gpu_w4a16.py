@@ -108,17 +108,23 @@ def test_zero_point_columns_are_exact(g, ws, asym, sched):
         check_against_oracle(p, D, what=f"{kname} zero-point groups {sched}")
 
 
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
 @pytest.mark.parametrize("K", [128, 384, 1152])
-def test_odd_group_count_ignores_scale_padding(g, ws, K):
+def test_odd_group_count_ignores_scale_padding(g, ws, K, asym):
     # an odd number of 128-deep groups leaves the second group of the last
     # k-tile past K; its scale slot holds the row padding, poisoned here with
-    # fp16 NaN, which must not reach the result
-    p = synth.w4a16_problem(33, 264, K, seed=K + 7)
+    # fp16 NaN, which must not reach the result (nor may the zero-point
+    # padding, poisoned with 0x7F bytes, in the asymmetric case)
+    p = synth.w4a16_problem(33, 264, K, seed=K + 7, asym=asym)
     r = Run(g, p, ws)
     G = K // 128
     assert r.ldv > G
     r.V[:, G:] = 0x7E00  # fp16 quiet NaN bit pattern (the device tensor holds int16 bits)
+    if asym:
+        assert r.U.shape[1] > G
+        r.U[:, G:] = 0x7F
     for kname in W4_KERNELS:
         for op in (r.op(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP, kernel=kidx(kname)),
+                   r.op(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=3, kernel=kidx(kname)),
                    r.op(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=5, kernel=kidx(kname))):
-            check_against_oracle(p, r.run(op), what=f"{kname} K={K}")
+            check_against_oracle(p, r.run(op), what=f"{kname} K={K} asym={asym} {r.plan(op)}")
