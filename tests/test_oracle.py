@@ -3,7 +3,6 @@
 matmul, invariants), so that a dropped term, a wrong sign or index, or a
 transposed operand in `oracle.c` fails at least one of them."""
 import json
-import os
 from fractions import Fraction
 import itertools
 
@@ -13,8 +12,6 @@ import torch
 
 import oracle
 import synth
-
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _dense(M, N, K, A, B, in_dtype="bf16", C=None, c_dtype=None, alpha=1.0, beta=0.0, out="f32"):
