@@ -18,7 +18,6 @@ self-check (contiguous K chunks summed in fp64, then in order).
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import subprocess
 

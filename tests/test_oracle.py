@@ -2,7 +2,6 @@
 (library decoders, closed forms, exact rational arithmetic, numpy's fp64 / int64
 matmul, invariants), so that a dropped term, a wrong sign or index, or a
 transposed operand in `oracle.c` fails at least one of them."""
-import json
 from fractions import Fraction
 import itertools
 
