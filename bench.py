@@ -270,6 +270,41 @@ class Workload:
         return t
 
 
+def timeline(runs, op, launches=30):
+    """Where the time of one split-K launch goes: qg_run_timed (the same plan,
+    kernel and result as qg_run) launched `launches` times back to back over
+    the workload's rotating input sets (as in the timed replays, so that the
+    caches see the same stream); the last launch's per-unit timestamps
+    (100 MHz clock) are summarised in microseconds. `mainloop_end_us` is when
+    the last unit's mainloop ended, counted from the first unit's start;
+    `fixup_read_us` and `store_us` are over the units that completed a tile."""
+    import numpy as np
+    import torch
+    import quantized_gemm_bf16_amd as qg
+    st, units = runs[0].launch_timed(op, None)
+    if units <= 0:
+        return None
+    stamps = torch.full((units * 8,), -1, dtype=torch.int64, device="cuda")
+    for i in range(launches):
+        st, _ = runs[i % len(runs)].launch_timed(op, stamps)
+        if st != qg.OK:
+            raise qg.QGemmError(st, "qg_run_timed")
+    torch.cuda.synchronize()
+    s = stamps.view(units, 8).cpu().numpy().astype(np.float64)
+    done = s[:, 5] == 1
+    t0 = s[:, 0].min()
+    end = np.where(done, s[:, 4], s[:, 2])
+    us = lambda x: round(float(x) / 100.0, 3)
+    return {"units": int(units), "completing_units": int(done.sum()),
+            "span_us": us(end.max() - t0), "last_start_us": us(s[:, 0].max() - t0),
+            "mainloop_us_mean": us((s[:, 1] - s[:, 0]).mean()), "mainloop_us_max": us((s[:, 1] - s[:, 0]).max()),
+            "mainloop_end_us": us(s[:, 1].max() - t0), "arrive_us_mean": us((s[:, 2] - s[:, 1]).mean()),
+            "fixup_read_us": us((s[done, 3] - s[done, 2]).mean()), "store_us": us((s[done, 4] - s[done, 3]).mean()),
+            "shader_clock_ghz": round(float(((s[:, 7] - s[:, 6]) / ((end - s[:, 0]) * 10.0)).mean()), 3),
+            "method": "qg_run_timed, 8 timestamps per split-K unit, last of %d launches over %d input sets"
+                      % (launches, len(runs))}
+
+
 def ceiling_mfma(dev, grid=256, iters=2048, steps=20):
     """MFMA-only loop at one 8-wave workgroup per CU: sustained bf16 rate and
     the shader clock measured inside the loop."""
@@ -491,6 +526,9 @@ def main():
                              plan=dw.runs[0].plan(op), clocks=t.get("clocks"),
                              kernel=dw.runs[0].plan(op).split()[0].split("=")[1])
             log(f"decode {name} {t['kernel_ms_mean'] * 1e3:.2f} us per launch")
+            if name == "splitk8":
+                res[name]["timeline"] = timeline(dw.runs, op)
+                log(f"decode {name} timeline {res[name]['timeline']}")
             if cpu and name == "splitk8":
                 oracle_cfg["decode_16x4096x14336_bf16"] = oracle_rows_time(dw.runs[0].p)
             del dw
@@ -510,6 +548,9 @@ def main():
                         "bytes_per_call": w4_bytes, "plan": ww.runs[0].plan(), "clocks": t.get("clocks")}
         kn = ww.runs[0].plan().split()[0].split("=")[1]
         out["w4a16"]["traffic"] = traffic_from_profile(kn, "w4a16_64x8192x8192")
+        if "schedule=splitk" in out["w4a16"]["plan"]:
+            out["w4a16"]["timeline"] = timeline(ww.runs, ww.op)
+            log(f"w4a16 timeline {out['w4a16']['timeline']}")
         if cpu:
             oracle_cfg["w4a16_64x8192x8192"] = oracle_rows_time(ww.runs[0].p)
         del ww

@@ -33,7 +33,7 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3, "i8": I8, "i3
 EXPORTS = ["qg_create", "qg_destroy", "qg_barriers_size", "qg_partials_size", "qg_run", "qg_plan",
            "qg_export", "qg_import", "qg_get_tuning_seq", "qg_cache_size", "qg_kernel_count",
            "qg_kernel_name", "qg_status_str", "qg_version", "qg_streamk_units", "qg_streamk_fixup",
-           "qg_run_noalloc", "qg_noalloc_barriers_size", "qg_noalloc_partials_size"]
+           "qg_run_noalloc", "qg_noalloc_barriers_size", "qg_noalloc_partials_size", "qg_run_timed"]
 
 
 class Layout(ctypes.Structure):
@@ -88,6 +88,9 @@ def _load(path=LIB_PATH):
                          P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout), P(Workspace), vp]
     L.qg_run_noalloc.argtypes = [vp, P(Operation), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp, P(Layout),
                                  vp, P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp]
+    L.qg_run_timed.argtypes = [vp, P(Operation), ctypes.c_float, vp, P(Layout), vp, P(Layout), vp, P(Layout), vp,
+                               P(Layout), ctypes.c_float, vp, P(Layout), vp, P(Layout), P(Workspace), vp,
+                               vp, ctypes.c_int64, P(ctypes.c_int64)]
     L.qg_noalloc_barriers_size.restype = sz
     L.qg_noalloc_partials_size.restype = sz
     L.qg_plan.argtypes = [vp, P(Operation), P(Layout), P(Layout), P(Layout), P(Layout), P(Layout), P(Layout),
@@ -104,7 +107,8 @@ def _load(path=LIB_PATH):
     L.qg_version.restype = ctypes.c_char_p
     L.qg_streamk_units.argtypes = [i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
     L.qg_streamk_fixup.argtypes = [i32, i32, i32, i32, P(ctypes.c_int32), i32, P(i32)]
-    for name in ("qg_create", "qg_destroy", "qg_run", "qg_run_noalloc", "qg_plan", "qg_export", "qg_import",
+    for name in ("qg_create", "qg_destroy", "qg_run", "qg_run_noalloc", "qg_run_timed", "qg_plan", "qg_export",
+                 "qg_import",
                  "qg_get_tuning_seq", "qg_cache_size", "qg_streamk_units", "qg_streamk_fixup"):
         getattr(L, name).restype = i32
     return L
@@ -229,6 +233,19 @@ class Gemm:
         return lib.qg_run_noalloc(self.h, ctypes.byref(op), float(alpha), _ptr(A), r(Ad), _ptr(U), r(Ud), _ptr(B),
                                   r(Bd), _ptr(V), r(Vd), float(beta), _ptr(C), r(Cd), _ptr(D), r(Dd),
                                   stream if stream is not None else _current_stream())
+
+    def run_timed_raw(self, op, alpha, A, Ad, U, Ud, B, Bd, V, Vd, beta, C, Cd, D, Dd, ws, stamps, units_cap,
+                      stream=None):
+        """qg_run_timed: a split-K run that writes 8 timestamps per split-K unit to
+        the device buffer `stamps` (units_cap units). Returns (status, units)."""
+        def r(x):
+            return None if x is None else ctypes.byref(x)
+        n = ctypes.c_int64()
+        st = lib.qg_run_timed(self.h, ctypes.byref(op), float(alpha), _ptr(A), r(Ad), _ptr(U), r(Ud), _ptr(B),
+                              r(Bd), _ptr(V), r(Vd), float(beta), _ptr(C), r(Cd), _ptr(D), r(Dd), r(ws),
+                              stream if stream is not None else _current_stream(), _ptr(stamps), int(units_cap),
+                              ctypes.byref(n))
+        return st, n.value
 
     def plan(self, op, Ad, Ud, Bd, Vd, Cd, Dd, alpha, beta, ws=None) -> str:
         buf = ctypes.create_string_buffer(512)

@@ -49,6 +49,10 @@ struct Args {
   int32_t grid;              // workgroups launched
   int32_t* counters;         // barriers workspace: one int32 per output tile
   void* partials;            // partials workspace
+
+  // measurement (split-K only, set by qg_run_timed; null otherwise): 8
+  // timestamps per split-K unit, see Sched::run_splitk
+  uint64_t* stamps;
 };
 
 }  // namespace qg

@@ -902,6 +902,31 @@ int qg_run(qg_handle* h, const qg_operation* op, float alpha, const void* A, con
   return launch(pl, stream);
 }
 
+int qg_run_timed(qg_handle* h, const qg_operation* op, float alpha, const void* A, const qg_layout* Adesc,
+                 const void* U, const qg_layout* Udesc, const void* B, const qg_layout* Bdesc, const void* V,
+                 const qg_layout* Vdesc, float beta, const void* C, const qg_layout* Cdesc, void* D,
+                 const qg_layout* Ddesc, const qg_workspace* ws, hipStream_t stream, uint64_t* stamps,
+                 int64_t units_cap, int64_t* units) {
+  if (!h || !op) return QG_ERR_INVALID_ARG;
+  if (units) *units = 0;
+  // measuring creates events and synchronises; the timeline is of one launch
+  if (op->policy == QG_POLICY_MEASURE) return QG_ERR_UNSUPPORTED;
+  Problem p;
+  int st = validate(op, alpha, A, Adesc, U, Udesc, B, Bdesc, V, Vdesc, beta, C, Cdesc, D, Ddesc, p);
+  if (st != QG_OK) return st;
+  if (p.M == 0 || p.N == 0) return QG_ERR_UNSUPPORTED;  // nothing is launched, nothing to time
+  Plan pl;
+  st = resolve(h, op, p, ws, pl, h->online, stream);
+  if (st != QG_OK) return st;
+  if (pl.a.mode != MODE_SPLITK) return QG_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)pl.a.tiles_m * pl.a.tiles_n * pl.a.splits;
+  if (units) *units = n;
+  if (!stamps || (uintptr_t)stamps % 8 != 0 || units_cap < n) return QG_ERR_INVALID_ARG;
+  pl.a.stamps = stamps;
+  if (!h->online) return QG_ERR_HIP;
+  return launch(pl, stream);
+}
+
 int qg_plan(qg_handle* h, const qg_operation* op, const qg_layout* Adesc, const qg_layout* Udesc,
             const qg_layout* Bdesc, const qg_layout* Vdesc, const qg_layout* Cdesc, const qg_layout* Ddesc, float alpha,
             float beta, const qg_workspace* ws, char* desc, size_t cap) {

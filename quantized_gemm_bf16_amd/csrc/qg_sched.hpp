@@ -149,19 +149,55 @@ struct Sched {
     }
   }
 
+  // Measurement only (a.stamps set by qg_run_timed): thread 0 records for
+  // split-K unit b, at stamps[8 b + i], the constant 100 MHz clock at
+  // i = 0 the unit's start, 1 the end of its mainloop, 2 after arrive,
+  // 3 once all waves of the completing unit have read the partials back and
+  // summed them (0 in the other units), 4 after its stores have completed
+  // (= [2] in the other units),
+  // 5 = 1 in the completing unit, and the shader clock at 6 (start) and 7
+  // (end). Uniform branches on a kernel argument, outside the mainloop.
+  __device__ __forceinline__ static void stamp(const Args& a, int b, int i, uint64_t v) {
+    if (a.stamps && threadIdx.x == 0) a.stamps[(size_t)b * 8 + i] = v;
+  }
+
   __device__ __forceinline__ static void run_splitk(const Args& a, char* smem, int* flag) {
     const int total = a.tiles_m * a.tiles_n * a.splits;
     for (int b = blockIdx.x; b < total; b += gridDim.x) {
       const int t = b / a.splits, s = b % a.splits;
       const int kb = s * a.iters_per_split, ke = min(a.iters, kb + a.iters_per_split);
+      if (a.stamps) {
+        stamp(a, b, 0, __builtin_amdgcn_s_memrealtime());
+        stamp(a, b, 6, __builtin_amdgcn_s_memtime());
+      }
       Acc acc;
       Unit u = make_unit(a, t, kb, ke);
       Core::mainloop(a, u, smem, acc);
-      if (arrive(a, u, t * a.splits + s, acc, flag)) {
+      if (a.stamps) stamp(a, b, 1, __builtin_amdgcn_s_memrealtime());
+      const bool last = arrive(a, u, t * a.splits + s, acc, flag);
+      uint64_t t2 = 0;
+      if (a.stamps) stamp(a, b, 2, t2 = __builtin_amdgcn_s_memrealtime());
+      if (last) {
         const int ns = (a.iters + a.iters_per_split - 1) / a.iters_per_split;
         reduce(a, ns, [&](int q) { return t * a.splits + q; }, acc);
+        if (a.stamps) {
+          __syncthreads();  // every wave has its partial tiles summed
+          stamp(a, b, 3, __builtin_amdgcn_s_memrealtime());
+        }
         Core::store(a, u, acc, smem);
         finish_counter(a, u);
+      }
+      if (a.stamps) {
+        if (last) {
+          wait_vmcnt<0>();
+          __syncthreads();
+          stamp(a, b, 4, __builtin_amdgcn_s_memrealtime());
+        } else {
+          stamp(a, b, 3, 0);
+          stamp(a, b, 4, t2);
+        }
+        stamp(a, b, 5, last ? 1 : 0);
+        stamp(a, b, 7, __builtin_amdgcn_s_memtime());
       }
     }
   }

@@ -116,6 +116,25 @@ void dense_plans(qg_handle* h) {
       const int st2 = qg_run_noalloc(h, &op, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, beta,
                                      kFake, &C, const_cast<void*>(kFake), &D, nullptr);
       EXPECT(st2 != QG_OK);
+      // the timed run: every schedule and split, short, missing and
+      // misaligned stamp buffers (offline, nothing is launched)
+      uint64_t* stamps = reinterpret_cast<uint64_t*>(const_cast<void*>(kFake));
+      for (int sc : scheds)
+        for (int split : {0, 1, 3, 8, 1000000}) {
+          const qg_operation top = opn(sc == QG_SCHED_AUTO ? QG_POLICY_DEFAULT : QG_POLICY_FORCE, sc, split, 7);
+          for (int64_t cap : {int64_t(-1), int64_t(0), int64_t(1), int64_t(1) << 40}) {
+            int64_t units = -5;
+            const int st3 = qg_run_timed(h, &top, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, beta,
+                                         kFake, &C, const_cast<void*>(kFake), &D, &ws, nullptr, stamps, cap, &units);
+            EXPECT(st3 != QG_OK && units >= 0);
+            EXPECT(qg_run_timed(h, &top, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, beta, kFake,
+                                &C, const_cast<void*>(kFake), &D, &ws, nullptr, nullptr, cap, nullptr) != QG_OK);
+            EXPECT(qg_run_timed(h, &top, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, beta, kFake,
+                                &C, const_cast<void*>(kFake), &D, &ws, nullptr,
+                                reinterpret_cast<uint64_t*>(reinterpret_cast<uintptr_t>(kFake) + 4), cap,
+                                &units) != QG_OK);
+          }
+        }
     }
 }
 
@@ -216,6 +235,11 @@ void invalid_requests(qg_handle* h) {
   EXPECT(run(&split8, kFake, &Ak, &Bk, &Dk, 0.f, nullptr, &tiny) == QG_ERR_WORKSPACE);
   EXPECT(qg_run(nullptr, &op, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, 0.f, nullptr, nullptr,
                 Dp, &D, &ws, nullptr) == QG_ERR_INVALID_ARG);
+  int64_t units = 0;
+  EXPECT(qg_run_timed(nullptr, &op, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, 0.f, nullptr,
+                      nullptr, Dp, &D, &ws, nullptr, nullptr, 0, &units) == QG_ERR_INVALID_ARG);
+  EXPECT(qg_run_timed(h, nullptr, 1.f, kFake, &A, nullptr, nullptr, kFake, &B, nullptr, nullptr, 0.f, nullptr,
+                      nullptr, Dp, &D, &ws, nullptr, nullptr, 0, &units) == QG_ERR_INVALID_ARG);
 }
 
 // xorshift64*: a fixed pseudo-random sequence for the import fuzzing

@@ -171,6 +171,15 @@ class Run:
                             self.Dd, self.ws.desc if self.ws is not None else None)
         return st
 
+    def launch_timed(self, op, stamps):
+        """qg_run_timed with this problem's operands; stamps: device int64
+        tensor of 8 * units entries. Returns (status, units)."""
+        p = self.p
+        return self.g.run_timed_raw(op, p["alpha"], self.A, self.Ad, self.U, self.Ud, self.B, self.Bd, self.V,
+                                    self.Vd, p["beta"], self.C, self.Cd, self.D, self.Dd,
+                                    self.ws.desc if self.ws is not None else None, stamps,
+                                    stamps.numel() // 8 if stamps is not None else 0)
+
     def run(self, op=None, **kw):
         # poison the partials workspace: a split-K / stream-K fixup that read
         # a slot before (or without) it being written would pick up NaNs
@@ -179,6 +188,14 @@ class Run:
         st = self.launch(op, **kw)
         if st != qg.OK:
             raise qg.QGemmError(st, "qg_run")
+        return self.run_result()
+
+    def reset_output(self):
+        """Refill D (valid columns and the pitch padding) with its sentinel."""
+        self.D.fill_(-7 if self.out in ("i32", "i8") else float("nan"))
+
+    def run_result(self):
+        """D after the launch (synchronises), with the padding checked untouched."""
         torch.cuda.synchronize()
         D = host_f64(self.D)
         pad = D[:, self.p["N"]:]

@@ -155,6 +155,34 @@ def test_workspace_checks(g):
     assert "schedule=dp" in desc
 
 
+def test_run_timed_argument_checks(g):
+    # qg_run_timed: split-K plans only, a stamps buffer of 8 x 8 bytes per
+    # split-K unit; the unit count comes back even when the buffer is short
+    Ad, Bd, Dd = dense(16, 4096, 14336)
+    op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
+
+    def timed(op, stamps, cap, ws=ws_desc()):
+        return g.run_timed_raw(op, 1.0, FAKE, Ad, None, None, FAKE, Bd, None, None, 0.0, None, None, FAKE, Dd, ws,
+                               stamps, cap)
+    d = dict(kv.split("=") for kv in g.plan(op, Ad, None, Bd, None, None, Dd, 1.0, 0.0, ws_desc()).split())
+    units = int(d["tiles"]) * 8
+    assert timed(op, FAKE, units - 1) == (qg.ERR_INVALID_ARG, units)
+    assert timed(op, None, units) == (qg.ERR_INVALID_ARG, units)
+    assert timed(op, FAKE + 4, units) == (qg.ERR_INVALID_ARG, units)
+    # a valid request: without a GPU the handle is offline
+    st, n = timed(op, FAKE, units)
+    assert n == units and st in (qg.ERR_HIP, qg.OK)
+    # not split-K, measuring, or nothing to launch
+    dp = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP)
+    assert timed(dp, FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
+    assert timed(qg.operation(policy=qg.POLICY_MEASURE), FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
+    Ad0, Bd0, Dd0 = dense(0, 4096, 14336)
+    assert g.run_timed_raw(op, 1.0, FAKE, Ad0, None, None, FAKE, Bd0, None, None, 0.0, None, None, FAKE, Dd0,
+                           ws_desc(), FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
+    # the request itself is validated first
+    assert timed(op, FAKE, units, ws=ws_desc(p=1024))[0] == qg.ERR_WORKSPACE
+
+
 def test_plan_decode_split8(g):
     Ad, Bd, Dd = dense(16, 4096, 14336)
     op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
