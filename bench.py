@@ -463,6 +463,8 @@ def main():
                     default=None, help="time one workload only (profiling)")
     ap.add_argument("--no-extra", action="store_true", help="skip the W4A16 and MoE workloads")
     ap.add_argument("--no-clocks", action="store_true", help="skip the sustained replay with clock sampling")
+    ap.add_argument("--no-timeline", action="store_true",
+                    help="skip the qg_run_timed launches (profiling: the timed replay's dispatches come last)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -526,7 +528,7 @@ def main():
                              plan=dw.runs[0].plan(op), clocks=t.get("clocks"),
                              kernel=dw.runs[0].plan(op).split()[0].split("=")[1])
             log(f"decode {name} {t['kernel_ms_mean'] * 1e3:.2f} us per launch")
-            if name == "splitk8":
+            if name == "splitk8" and not args.no_timeline:
                 res[name]["timeline"] = timeline(dw.runs, op)
                 log(f"decode {name} timeline {res[name]['timeline']}")
             if cpu and name == "splitk8":
@@ -548,7 +550,7 @@ def main():
                         "bytes_per_call": w4_bytes, "plan": ww.runs[0].plan(), "clocks": t.get("clocks")}
         kn = ww.runs[0].plan().split()[0].split("=")[1]
         out["w4a16"]["traffic"] = traffic_from_profile(kn, "w4a16_64x8192x8192")
-        if "schedule=splitk" in out["w4a16"]["plan"]:
+        if "schedule=splitk" in out["w4a16"]["plan"] and not args.no_timeline:
             out["w4a16"]["timeline"] = timeline(ww.runs, ww.op)
             log(f"w4a16 timeline {out['w4a16']['timeline']}")
         if cpu:
