@@ -456,7 +456,50 @@ struct W4 {
   // ever indexed with compile-time indices (loops over every tn with this
   // uniform test): a wave-dependent index would send them to scratch.
   __device__ __forceinline__ static bool keeps(int tn) { return tn / TO == wk_of(wave_id()); }
-  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* /*smem*/) {
+  // A whole tile with a plain 16-bit D (no C term, no fused epilogue) goes
+  // out through LDS: the waves round their kept n-tiles into a BM x BN tile
+  // (rows padded by 16 bytes, so that the 16 rows of a lane group's 8-byte
+  // writes fall in different banks), then every thread writes whole 16-byte
+  // pieces of 2*BN-byte rows, instead of 8-byte pieces of 16 rows per store.
+  static constexpr int SROW = BN * 2 + 16;
+  static_assert(BM * SROW <= Cfg::SMEM, "staging tile");
+  __device__ __forceinline__ static void store_staged(const Args& a, const Unit& u, Acc& acc, char* smem) {
+    const int w = wave_id(), l = lane_id();
+    const int wn = wn_of(w);
+    const bool bf = a.d_type == DT_BF16;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 16 + (l & 15);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if (!keeps(tn)) continue;
+        const int col = wn * BNW + tn * 16 + 4 * (l >> 4);
+        uint16_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = a.alpha * acc.v[tn][mt][j];
+          h[j] = bf ? f32_to_bf16_bits(x) : f32_to_f16_bits(x);
+        }
+        *(u16x4*)(smem + row * SROW + col * 2) = u16x4{h[0], h[1], h[2], h[3]};
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = BN * 2 / 16;  // 16-byte pieces per row
+    for (int idx = (int)threadIdx.x; idx < BM * CPR; idx += NT) {
+      const int row = idx / CPR, ch = idx % CPR;
+      const i32x4 v = *(const i32x4*)(smem + row * SROW + ch * 16);
+      uint16_t* p = (uint16_t*)a.D + (int64_t)(u.m0 + row) * a.ldd + u.n0 + ch * 8;
+      __builtin_nontemporal_store(v, (i32x4*)p);
+    }
+    __syncthreads();  // the staging area is the next unit's ring
+  }
+
+  __device__ __forceinline__ static void store(const Args& a, const Unit& u, Acc& acc, char* smem) {
+    const bool plain16 = (a.d_type == DT_BF16 || a.d_type == DT_F16) && (a.c_type < 0 || a.beta == 0.f) && a.epi == 0;
+    if (plain16 && u.m0 + BM <= u.m_end && u.n0 + BN <= a.N) {
+      store_staged(a, u, acc, smem);
+      return;
+    }
     const int w = wave_id(), l = lane_id();
     const int wn = wn_of(w);
 #pragma unroll
