@@ -14,6 +14,8 @@ _TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16
 def dev(arr):
     """numpy array (any bit pattern) -> contiguous device tensor holding the same bytes."""
     a = np.ascontiguousarray(arr)
+    if not a.flags.writeable:  # e.g. a broadcast view; torch wants a writable buffer
+        a = a.copy()
     if a.dtype == np.uint16:
         a = a.view(np.int16)
     elif a.dtype == np.uint32:

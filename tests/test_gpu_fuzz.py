@@ -94,3 +94,56 @@ def test_fuzz_case(env, i):
     D = r.run(op)
     check_against_oracle(p, D, what=what)
     assert int(ws.barriers.abs().sum().item()) == 0, f"{what}: arrival counters not left zero"
+
+
+# Grouped (MoE: per-expert row counts, some experts empty) and batched
+# (equal batches, B per batch or shared) problems, with the engine's plan.
+GROUPED_CASES = 100
+GROUPED_KINDS = ["grouped", "grouped_fp8", "batched", "batched_fp8", "batched_i8"]
+
+
+def draw_grouped(i):
+    r = np.random.default_rng(9000 + i)
+    kind = GROUPED_KINDS[i % len(GROUPED_KINDS)]
+    N = int(r.integers(1, 401))
+    seed = 500 + i
+    if kind.startswith("grouped"):
+        E = int(r.integers(1, 25))
+        counts = r.integers(0, 300, size=E)
+        counts[r.random(E) < 0.25] = 0
+        if counts.sum() == 0:
+            counts[0] = 1
+        K = int(r.integers(1, 901))
+        out = str(r.choice(["bf16", "f32"]))
+        p = synth.grouped_problem(counts, N, K, in_dtype=str(r.choice(["bf16", "f16"])), out_dtype=out, seed=seed,
+                                  fp8=kind == "grouped_fp8")
+        return kind, p
+    batch, M, K = int(r.integers(1, 9)), int(r.integers(1, 130)), 16 * int(r.integers(1, 50))
+    use_c = bool(r.integers(0, 2))
+    if kind == "batched_i8":
+        p = synth.batched_problem(batch, M, N, K, in_dtype="i8", c_dtype="i32" if use_c else None, beta=1.0,
+                                  seed=seed)
+    else:
+        fp8 = kind == "batched_fp8"
+        p = synth.batched_problem(batch, M, N, K, in_dtype="bf16", out_dtype=str(r.choice(["bf16", "f32"])),
+                                  c_dtype=str(r.choice(["bf16", "f32"])) if use_c else None,
+                                  alpha=float(r.choice([1.0, -0.5])), beta=float(r.choice([0.5, 1.0])) if use_c else 0.0,
+                                  seed=seed, share_b=bool(r.integers(0, 2)), fp8=fp8)
+    return kind, p
+
+
+@pytest.mark.parametrize("i", range(GROUPED_CASES))
+def test_fuzz_grouped_case(env, i):
+    g, ws = env
+    kind, p = draw_grouped(i)
+    if kind.startswith("grouped"):
+        per = 16 if p["in_dtype"] == "e4m3" else 8
+        r = Run(g, p, ws, ldk=-(-p["K"] // per) * per)
+    else:
+        r = Run(g, p, ws)
+    op = r.op()
+    what = f"grouped case {i}: {kind} E={p['E']} rows={p['M']} N={p['N']} K={p['K']} out={p['out_dtype']} " \
+           f"c={p.get('c_dtype')} | {r.plan(op)}"
+    print(what, flush=True)
+    D = r.run(op)
+    check_against_oracle(p, D, what=what)
