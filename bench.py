@@ -346,6 +346,60 @@ def ceiling_stream(dev, nbytes, nsets=3, steps=30):
     return best
 
 
+def issue_overlap(grid=256, iters=4096):
+    """Shader cycles per round of qgc_issue_mix, until both waves of a SIMD
+    are done: four 16x16x32 bf16 MFMAs per wave alone, sixteen VALU
+    instructions of one kind per wave alone, and both interleaved; `hidden`
+    is the share of the MFMA-only time that the VALU work hides,
+    (mfma + valu - both) / mfma."""
+    import torch
+    from quantized_gemm_bf16_amd import ceiling as qc
+    sink = torch.empty(grid, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(grid, dtype=torch.int64, device="cuda")
+
+    def cycles(mode, kind):
+        for _ in range(3):
+            qc.issue_mix(mode, kind, grid, iters, sink, clk)
+        torch.cuda.synchronize()
+        return float(clk.double().mean()) / iters
+
+    mf = cycles(1, 0)
+    out = {"mfma": round(mf, 1)}
+    for kind, name in qc.ISSUE_KINDS.items():
+        v, b = cycles(2, kind), cycles(3, kind)
+        out[name] = round(v, 1)
+        out[name + "+mfma"] = round(b, 1)
+        out["hidden_" + name] = round((mf + v - b) / mf, 3)
+    out["unit"] = (f"shader cycles per round until both waves of a SIMD are done; a round is, per wave, "
+                   f"{qc.ISSUE_MFMA_PER_ROUND} v_mfma_f32_16x16x32_bf16 and/or {qc.ISSUE_VALU_PER_ROUND} VALU "
+                   f"instructions of the kind")
+    return out
+
+
+def graph_launch_floor(launches=100, reps=3):
+    """Device time per launch of an empty kernel replayed from a HIP graph
+    (the floor under every graph-replayed GEMM launch); median of reps."""
+    import torch
+    from quantized_gemm_bf16_amd import ceiling as qc
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qc.empty()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(launches):
+                qc.empty()
+        xs = []
+        for _ in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            e1.synchronize()
+            xs.append(e0.elapsed_time(e1) * 1e3 / launches)
+    return round(statistics.median(xs[2:]), 3)
+
+
 def host_timing(g, ws, n=500):
     """Host microseconds per qg_run on the decode problem (M=16), from a C loop
     of n back-to-back calls; median of three loops."""
@@ -581,6 +635,10 @@ def main():
         log(f"mfma ceiling {out['ceilings']['mfma_bf16']['tflops']} TFLOP/s")
         out["ceilings"]["stream_read"] = ceiling_stream(dev, 4096 * 14336 * 2)
         log(f"stream ceiling {out['ceilings']['stream_read']['GB/s']} GB/s")
+        out["ceilings"]["issue_overlap"] = issue_overlap()
+        log(f"issue overlap {out['ceilings']['issue_overlap']}")
+        out["ceilings"]["graph_launch_floor_us"] = graph_launch_floor()
+        log(f"graph launch floor {out['ceilings']['graph_launch_floor_us']} us")
     if only in (None, "host"):
         out["host_us_per_call"] = host_timing(g, ws)
         log(f"host {out['host_us_per_call']}")

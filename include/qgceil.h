@@ -7,6 +7,7 @@
  *   - an MFMA-only loop at the GEMM kernels' occupancy (the sustained matrix
  *     rate, and the shader clock it ran at);
  *   - a streaming read (the sustained HBM read rate);
+ *   - how far vector work overlaps matrix work on one SIMD;
  *   - empty kernels (the runtime's launch cost, without and with a kernel
  *     argument block);
  *   - a host loop that times calls of a qg_run-shaped function.
@@ -54,6 +55,26 @@ int qgc_mfma_loop(int grid, int iters, float* sink, uint64_t* clk, hipStream_t s
  * read to sink[thread] (grid * 256 dwords), so the XOR of the whole sink is
  * the XOR of the buffer's dwords. 1 <= grid <= 65535. */
 int qgc_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, hipStream_t stream);
+
+/* Issue overlap of matrix and vector work on one SIMD: `grid` workgroups
+ * shaped like qgc_mfma_loop's (8 waves, 96 KiB of LDS, so two waves share
+ * each SIMD). Every wave runs `iters` rounds; a round holds, interleaved one
+ * MFMA to four VALU instructions,
+ *   mode 1: four v_mfma_f32_16x16x32_bf16 on independent accumulators,
+ *   mode 2: sixteen VALU instructions of one kind on eight independent
+ *           chains,
+ *   mode 3: both;
+ * the VALU kind is 0: fp32 fused multiply-add (v_fma_f32); 1: the int4
+ * unpack's bitwise pair (a byte permute and an and-or, eight pairs);
+ * 2: fp32 fused multiply-add with an fp16 operand (v_fma_mix_f32).
+ *   sink: grid floats (device), one value per workgroup so that nothing is
+ *         optimised away;
+ *   clk:  grid uint64 (device): for each workgroup, shader-clock cycles
+ *         from the start of the rounds until all its waves have finished
+ *         them (a workgroup barrier; per SIMD that is two waves' rounds).
+ * 1 <= grid <= 65535, 1 <= iters <= 1 << 20, 1 <= mode <= 3, 0 <= kind <= 2
+ * (kind is ignored for mode 1). */
+int qgc_issue_mix(int mode, int kind, int grid, int iters, float* sink, uint64_t* clk, hipStream_t stream);
 
 /* One launch of an empty kernel (one workgroup of 64 threads). */
 int qgc_empty(hipStream_t stream);

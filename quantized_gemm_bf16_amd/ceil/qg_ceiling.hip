@@ -13,6 +13,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaThreads = 512;
 constexpr int kMfmaLds = 96 * 1024;  // > 80 KiB: one workgroup per CU
@@ -49,6 +50,87 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop(int iters, float* sink
     sink[blockIdx.x] = s + (float)((volatile char*)lds)[blockIdx.x % kMfmaLds];
     clk[2 * blockIdx.x] = t1 - t0;
     clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// Values the compiler cannot fold: the loop below must keep its constants
+// in registers (as the int4 unpack does) and its fp16 operand live.
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_sgpr() {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+  return r;
+}
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_vgpr() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
+  return r;
+}
+
+// One round: four slots of one MFMA (MODE bit 0) and four VALU instructions
+// (MODE bit 1). The eight VALU chains advance once every other slot, so a
+// chain's next instruction is eight instructions after its last one.
+template <int MODE, int KIND>
+__global__ __launch_bounds__(kMfmaThreads) void issue_mix(int iters, float* sink, uint64_t* clk) {
+  __shared__ char lds[kMfmaLds];
+  const int t = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)((float)((t + j) & 7) * 0.125f);
+    b[j] = (__bf16)((float)((t * 3 + j) & 7) * -0.0625f);
+  }
+  f32x4 acc[4] = {};
+  float x[8];
+  uint32_t u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = (float)t * 1e-3f + (float)j;
+    u[j] = (uint32_t)t * 0x9E3779B9u + (uint32_t)j;
+  }
+  const float y = __builtin_bit_cast(float, opaque_vgpr<0x3f7fbe77u>());  // 0.999
+  const float z = __builtin_bit_cast(float, opaque_vgpr<0x38d1b717u>());  // 1e-4
+  _Float16 h = (_Float16)(float)__builtin_bit_cast(float, opaque_vgpr<0x3c000000u>());  // 2^-7
+  const uint32_t m = opaque_sgpr<0x000F000Fu>(), c = opaque_vgpr<0x43004300u>();
+  const uint32_t sel = opaque_sgpr<0x0C040C00u>();
+  if (t == 0) ((volatile char*)lds)[blockIdx.x % kMfmaLds] = 1;  // keeps the LDS allocation
+  __syncthreads();
+  const uint64_t t0 = __builtin_readcyclecounter();
+  for (int i = 0; i < iters; ++i) {
+    // the fp16 operand as a new value each round (the statement emits
+    // nothing), so that the conversion is not hoisted out of the loop and the
+    // multiply-adds stay mixed-precision instructions
+    if constexpr (KIND == 2) asm volatile("" : "+v"(h));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (MODE & 1)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[q], 0, 0, 0);
+      if constexpr (MODE & 2) {
+        const int j0 = (q & 1) * 4;
+        if constexpr (KIND == 1) {
+#pragma unroll
+          for (int j = j0; j < j0 + 2; ++j) u[j] = (__builtin_amdgcn_perm(u[j], u[j], sel) & m) | c;
+        } else {
+#pragma unroll
+          for (int j = j0; j < j0 + 4; ++j)
+            x[j] = KIND == 0 ? __builtin_fmaf(x[j], y, z) : __builtin_fmaf((float)h, x[j], y);
+        }
+      }
+    }
+  }
+  // until every wave is done: the older wave of a SIMD wins the issue
+  // arbitration and finishes first, so one wave's own time would undercount
+  __syncthreads();
+  const uint64_t t1 = __builtin_readcyclecounter();
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s += acc[q][0] + acc[q][3];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j] + (float)(u[j] & 1);
+  if (t == 0) {
+    sink[blockIdx.x] = s + (float)((volatile char*)lds)[blockIdx.x % kMfmaLds];
+    clk[blockIdx.x] = t1 - t0;
   }
 }
 
@@ -103,6 +185,18 @@ int qgc_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, hip
     return QG_ERR_INVALID_ARG;
   hipLaunchKernelGGL(stream_read, dim3(grid), dim3(kStreamThreads), 0, stream, (const char*)src, (uint32_t)bytes,
                      sink);
+  return launched();
+}
+
+int qgc_issue_mix(int mode, int kind, int grid, int iters, float* sink, uint64_t* clk, hipStream_t stream) {
+  if (mode < 1 || mode > 3 || kind < 0 || kind > 2 || grid < 1 || grid > 65535 || iters < 1 || iters > (1 << 20) ||
+      !sink || !clk)
+    return QG_ERR_INVALID_ARG;
+  void (*k)(int, float*, uint64_t*) = nullptr;
+  if (mode == 1) k = issue_mix<1, 0>;
+  else if (mode == 2) k = kind == 0 ? issue_mix<2, 0> : (kind == 1 ? issue_mix<2, 1> : issue_mix<2, 2>);
+  else k = kind == 0 ? issue_mix<3, 0> : (kind == 1 ? issue_mix<3, 1> : issue_mix<3, 2>);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kMfmaThreads), 0, stream, iters, sink, clk);
   return launched();
 }
 

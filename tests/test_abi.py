@@ -52,6 +52,11 @@ def test_measurement_library_rejects_bad_arguments():
     assert L.qgc_stream_read(FAKE + 4, 16, 1, FAKE, None) == qg.ERR_INVALID_ARG
     assert L.qgc_stream_read(FAKE, 1 << 31, 1, FAKE, None) == qg.ERR_INVALID_ARG
     assert L.qgc_stream_read(FAKE, 16, 65536, FAKE, None) == qg.ERR_INVALID_ARG
+    for mode, kind, grid, iters in ((0, 0, 1, 1), (4, 0, 1, 1), (2, 3, 1, 1), (2, -1, 1, 1), (1, 0, 0, 1),
+                                    (1, 0, 65536, 1), (1, 0, 1, 0), (1, 0, 1, (1 << 20) + 1)):
+        assert L.qgc_issue_mix(mode, kind, grid, iters, FAKE, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_issue_mix(1, 0, 1, 1, None, FAKE, None) == qg.ERR_INVALID_ARG
+    assert L.qgc_issue_mix(1, 0, 1, 1, FAKE, None, None) == qg.ERR_INVALID_ARG
     out = ctypes.c_double()
     assert L.qgc_host_us_per_empty(0, 0, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG
     assert L.qgc_host_us_per_empty(1, 8, None, ctypes.byref(out)) == qg.ERR_INVALID_ARG

@@ -1,6 +1,8 @@
 """GPU checks of the measurement library (libqgceil.so) that the benchmark
 reports ceilings with: the streaming read covers every byte once, the MFMA
-loop reports a plausible clock and rate, the host loops return figures."""
+loop reports a plausible clock and rate, the issue-overlap loops report
+plausible cycle counts, the host loops and the graph launch floor return
+figures."""
 import numpy as np
 import pytest
 import torch
@@ -50,6 +52,31 @@ def test_mfma_loop_clock_and_rate(qc):
     # below the dense bf16 peak at the measured clock (4096 flop/clk/CU), and not absurdly low
     assert 100 < tflops <= 4096 * 256 * ghz * 1e9 / 1e12 * 1.02, (tflops, ghz)
     assert np.isfinite(sink.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_issue_mix_cycles(qc, kind):
+    grid, iters = 256, 256
+    sink = torch.empty(grid, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(grid, dtype=torch.int64, device="cuda")
+    per = {}
+    for mode in (1, 2, 3):
+        qc.issue_mix(mode, kind, grid, iters, sink, clk)
+        torch.cuda.synchronize()
+        c = clk.cpu().double().numpy() / iters
+        assert (c > 0).all() and np.isfinite(sink.cpu().numpy()).all()
+        per[mode] = float(c.mean())
+    # two waves per SIMD, timed until both are done: a round is at least
+    # 2 waves x 4 MFMAs x 16 cycles; both together take at least each alone
+    # (10 % slack for run-to-run noise) and at most their sum plus slack
+    assert per[1] >= 0.9 * 128, per
+    assert per[3] >= 0.9 * max(per[1], per[2]) and per[3] <= 1.3 * (per[1] + per[2]), per
+
+
+def test_graph_launch_floor(qc):
+    import bench
+    us = bench.graph_launch_floor(launches=20, reps=2)
+    assert 0.05 < us < 100, us
 
 
 def test_host_loops(qc):
