@@ -270,14 +270,17 @@ class Workload:
         return t
 
 
-def timeline(runs, op, launches=30):
-    """Where the time of one split-K launch goes: qg_run_timed (the same plan,
-    kernel and result as qg_run) launched `launches` times back to back over
-    the workload's rotating input sets (as in the timed replays, so that the
-    caches see the same stream); the last launch's per-unit timestamps
-    (100 MHz clock) are summarised in microseconds. `mainloop_end_us` is when
-    the last unit's mainloop ended, counted from the first unit's start;
-    `fixup_read_us` and `store_us` are over the units that completed a tile."""
+def timeline(runs, op, launches=30, k_tiles=None):
+    """Where the time of one split-K or data-parallel launch goes:
+    qg_run_timed (the same plan, kernel and result as qg_run) launched
+    `launches` times back to back over the workload's rotating input sets (as
+    in the timed replays, so that the caches see the same stream); the last
+    launch's per-unit timestamps (100 MHz clock) are summarised in
+    microseconds. `mainloop_end_us` is when the last unit's mainloop ended,
+    counted from the first unit's start; `fixup_read_us` and `store_us` are
+    over the units that completed a tile. With `k_tiles` (k-tiles per unit),
+    `cycles_per_k_tile` is the mean mainloop time in shader cycles (each
+    unit's mainloop time at that unit's measured shader clock) per k-tile."""
     import numpy as np
     import torch
     import quantized_gemm_bf16_amd as qg
@@ -301,7 +304,9 @@ def timeline(runs, op, launches=30):
             "mainloop_end_us": us(s[:, 1].max() - t0), "arrive_us_mean": us((s[:, 2] - s[:, 1]).mean()),
             "fixup_read_us": us((s[done, 3] - s[done, 2]).mean()), "store_us": us((s[done, 4] - s[done, 3]).mean()),
             "shader_clock_ghz": round(float(((s[:, 7] - s[:, 6]) / ((end - s[:, 0]) * 10.0)).mean()), 3),
-            "method": "qg_run_timed, 8 timestamps per split-K unit, last of %d launches over %d input sets"
+            **({"cycles_per_k_tile": round(float(((s[:, 1] - s[:, 0]) * (s[:, 7] - s[:, 6]) / (end - s[:, 0])).mean())
+                                           / k_tiles, 1), "k_tiles_per_unit": int(k_tiles)} if k_tiles else {}),
+            "method": "qg_run_timed, 8 timestamps per unit, last of %d launches over %d input sets"
                       % (launches, len(runs))}
 
 
@@ -564,6 +569,11 @@ def main():
         log(f"square {t['kernel_ms_mean'] * 1e3:.1f} us per launch")
         out["square"] = dict(t, kernel=kname, plan=sq.runs[0].plan(), tflops=flops / (ms_step * 1e-3) / 1e12,
                              kernel_tflops=flops / (t["kernel_ms_mean"] * 1e-3) / 1e12)
+        pd = dict(kv.split("=") for kv in sq.runs[0].plan().split())
+        if pd["schedule"] in ("dp", "splitk") and not args.no_timeline:
+            kt = -(-(-(-K // int(pd["bk"]))) // int(pd["split"]))
+            out["square"]["timeline"] = timeline(sq.runs, sq.op, k_tiles=kt)
+            log(f"square timeline {out['square']['timeline']}")
         del sq
 
     if only in (None, "decode"):
@@ -675,6 +685,7 @@ def main():
                      "frac_of_sustained": round(achieved / mf["tflops"], 4),
                      "sustained_ceiling": "ceilings.mfma_bf16.tflops (MFMA-only loop, same process)"},
         "clocks": sq_.get("clocks"),
+        "timeline": sq_.get("timeline"),
         "ceilings": out["ceilings"],
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in out["decode"].items()
                    if not isinstance(v, dict)},

@@ -265,24 +265,27 @@ int qg_run_noalloc(qg_handle* h, const qg_operation* op, float alpha,
 size_t qg_noalloc_barriers_size(void);
 size_t qg_noalloc_partials_size(void);
 
-/* qg_run of a split-K plan that also records where the time of the launch
- * goes (measurement; the pages' tuning is by measurement -- Interface page,
- * Description). The plan, the kernel and its result are those of qg_run (the
- * same bits); in addition the first thread of the workgroup running split-K
- * unit u (tile t, chunk s; u = t * splits + s) writes eight 64-bit values to
- * stamps[8u .. 8u+7] (device memory, 8-byte aligned): the constant 100 MHz
- * clock at the unit's start [0], at the end of its mainloop [1], after it
- * published its partial tile [2], after the unit that completed the tile
- * read the partial tiles back and summed them (all its waves) [3] (0 in the
- * other units), after the completing unit's stores finished [4] (= [2] in
- * the other units), 1 in the completing unit and 0 otherwise [5], and the
- * shader clock at the start [6]
- * and end [7]. *units receives the number of split-K units of the plan (also
- * when the call fails for a short buffer); units_cap is the capacity of
- * `stamps` in units. Returns QG_ERR_UNSUPPORTED when the resolved plan is not
- * split-K, for QG_POLICY_MEASURE and for an empty problem, and
- * QG_ERR_INVALID_ARG for a missing, misaligned or short `stamps`; otherwise
- * as qg_run. */
+/* qg_run of a split-K or data-parallel plan that also records where the
+ * time of the launch goes (measurement; the pages' tuning is by measurement
+ * -- Interface page, Description). The plan, the kernel and its result are
+ * those of qg_run (the same bits); in addition the first thread of the
+ * workgroup running unit u writes eight 64-bit values to stamps[8u .. 8u+7]
+ * (device memory, 8-byte aligned). A split-K unit is (tile t, chunk s),
+ * u = t * splits + s; a data-parallel unit is tile u. The values: the
+ * constant 100 MHz clock at the unit's start [0], at the end of its
+ * mainloop [1], after it published its partial tile [2] (data-parallel: =
+ * [1]), after the unit that completed the tile read the partial tiles back
+ * and summed them (all its waves) [3] (0 in the other split-K units;
+ * data-parallel: = [1]), after the completing unit's stores finished [4]
+ * (= [2] in the split-K units that do not complete their tile), 1 in a unit
+ * that completes its tile (every data-parallel unit) and 0 otherwise [5],
+ * and the shader clock at the start [6] and end [7]. *units receives the
+ * number of units of the plan (also when the call fails for a short buffer);
+ * units_cap is the capacity of `stamps` in units. Returns
+ * QG_ERR_UNSUPPORTED when the resolved plan is neither split-K nor
+ * data-parallel (stream-K, grouped, batched), for QG_POLICY_MEASURE and for
+ * an empty problem, and QG_ERR_INVALID_ARG for a missing, misaligned or
+ * short `stamps`; otherwise as qg_run. */
 int qg_run_timed(qg_handle* h, const qg_operation* op, float alpha,
                  const void* A, const qg_layout* Adesc,
                  const void* U, const qg_layout* Udesc,

@@ -918,8 +918,8 @@ int qg_run_timed(qg_handle* h, const qg_operation* op, float alpha, const void* 
   Plan pl;
   st = resolve(h, op, p, ws, pl, h->online, stream);
   if (st != QG_OK) return st;
-  if (pl.a.mode != MODE_SPLITK) return QG_ERR_UNSUPPORTED;
-  const int64_t n = (int64_t)pl.a.tiles_m * pl.a.tiles_n * pl.a.splits;
+  if (pl.a.mode != MODE_SPLITK && pl.a.mode != MODE_DP) return QG_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)pl.a.tiles_m * pl.a.tiles_n * (pl.a.mode == MODE_SPLITK ? pl.a.splits : 1);
   if (units) *units = n;
   if (!stamps || (uintptr_t)stamps % 8 != 0 || units_cap < n) return QG_ERR_INVALID_ARG;
   pl.a.stamps = stamps;

@@ -138,27 +138,46 @@ struct Sched {
     return x * q + min(x, r) + (b >> 3);
   }
 
+  // Measurement only (a.stamps set by qg_run_timed): thread 0 records for
+  // unit b, at stamps[8 b + i], the constant 100 MHz clock at i = 0 the
+  // unit's start, 1 the end of its mainloop, 2 after arrive (split-K; the
+  // mainloop's end in a data-parallel unit, which publishes nothing),
+  // 3 once all waves of the completing unit have read the partials back and
+  // summed them (0 in the other split-K units; the mainloop's end in a
+  // data-parallel unit), 4 after its stores have completed (= [2] in the
+  // split-K units that do not complete their tile), 5 = 1 in a unit that
+  // completes its tile, and the shader clock at 6 (start) and 7 (end).
+  // Uniform branches on a kernel argument, outside the mainloop.
+  __device__ __forceinline__ static void stamp(const Args& a, int b, int i, uint64_t v) {
+    if (a.stamps && threadIdx.x == 0) a.stamps[(size_t)b * 8 + i] = v;
+  }
+
   __device__ __forceinline__ static void run_dp(const Args& a, char* smem) {
     const int total = a.tiles_m * a.tiles_n;
     for (int b = blockIdx.x; b < total; b += gridDim.x) {
       const int t = (gridDim.x == (unsigned)total) ? xcd_remap(b, total) : b;
+      if (a.stamps) {
+        stamp(a, t, 0, __builtin_amdgcn_s_memrealtime());
+        stamp(a, t, 6, __builtin_amdgcn_s_memtime());
+      }
       Acc acc;
       Unit u = make_unit(a, t, 0, a.iters);
       Core::mainloop(a, u, smem, acc);
+      if (a.stamps) {
+        const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+        stamp(a, t, 1, t1);
+        stamp(a, t, 2, t1);
+        stamp(a, t, 3, t1);
+      }
       Core::store(a, u, acc, smem);
+      if (a.stamps) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        stamp(a, t, 4, __builtin_amdgcn_s_memrealtime());
+        stamp(a, t, 5, 1);
+        stamp(a, t, 7, __builtin_amdgcn_s_memtime());
+      }
     }
-  }
-
-  // Measurement only (a.stamps set by qg_run_timed): thread 0 records for
-  // split-K unit b, at stamps[8 b + i], the constant 100 MHz clock at
-  // i = 0 the unit's start, 1 the end of its mainloop, 2 after arrive,
-  // 3 once all waves of the completing unit have read the partials back and
-  // summed them (0 in the other units), 4 after its stores have completed
-  // (= [2] in the other units),
-  // 5 = 1 in the completing unit, and the shader clock at 6 (start) and 7
-  // (end). Uniform branches on a kernel argument, outside the mainloop.
-  __device__ __forceinline__ static void stamp(const Args& a, int b, int i, uint64_t v) {
-    if (a.stamps && threadIdx.x == 0) a.stamps[(size_t)b * 8 + i] = v;
   }
 
   __device__ __forceinline__ static void run_splitk(const Args& a, char* smem, int* flag) {

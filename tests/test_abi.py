@@ -161,8 +161,9 @@ def test_workspace_checks(g):
 
 
 def test_run_timed_argument_checks(g):
-    # qg_run_timed: split-K plans only, a stamps buffer of 8 x 8 bytes per
-    # split-K unit; the unit count comes back even when the buffer is short
+    # qg_run_timed: split-K and data-parallel plans, a stamps buffer of
+    # 8 x 8 bytes per unit; the unit count comes back even when the buffer is
+    # short
     Ad, Bd, Dd = dense(16, 4096, 14336)
     op = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_SPLITK, split_k=8)
 
@@ -177,9 +178,16 @@ def test_run_timed_argument_checks(g):
     # a valid request: without a GPU the handle is offline
     st, n = timed(op, FAKE, units)
     assert n == units and st in (qg.ERR_HIP, qg.OK)
-    # not split-K, measuring, or nothing to launch
+    # data-parallel: one unit per tile
     dp = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_DP)
-    assert timed(dp, FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
+    tiles = int(dict(kv.split("=") for kv in g.plan(dp, Ad, None, Bd, None, None, Dd, 1.0, 0.0,
+                                                     ws_desc()).split())["tiles"])
+    assert timed(dp, FAKE, tiles - 1) == (qg.ERR_INVALID_ARG, tiles)
+    st, n = timed(dp, FAKE, tiles)
+    assert n == tiles and st in (qg.ERR_HIP, qg.OK)
+    # stream-K, measuring, or nothing to launch
+    sk = qg.operation(policy=qg.POLICY_FORCE, schedule=qg.SCHED_STREAMK, programs=64)
+    assert timed(sk, FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
     assert timed(qg.operation(policy=qg.POLICY_MEASURE), FAKE, 1 << 20)[0] == qg.ERR_UNSUPPORTED
     Ad0, Bd0, Dd0 = dense(0, 4096, 14336)
     assert g.run_timed_raw(op, 1.0, FAKE, Ad0, None, None, FAKE, Bd0, None, None, 0.0, None, None, FAKE, Dd0,
